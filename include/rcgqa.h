@@ -1,0 +1,164 @@
+/*
+ * rcgqa.h -- C ABI of librcgqa: rotary position embedding and causal
+ * grouped-query scaled-dot-product attention (prefill and single-token decode
+ * against a KV cache) on AMD MI355X (gfx950).
+ *
+ * Sources (titles and sections of the pages the method is taken from):
+ *   [HF]   "【HuggingFace Transformers】LlamaAttention源码解析" -- section 1.2 (attention
+ *          steps 1-5), section 2 (LlamaAttention.forward, steps 1-6).
+ *   [L2]   "LLaMA2大语言模型架构详解" -- sections "Rotary Position Encoding", "KV cache",
+ *          "Grouped Multi-Query Attention (GQA)".
+ *   [L2X]  "Llama2 Transformer架构解析与优化实践" -- sections 2.1, 3.2, 6.1.
+ *   [VERL] "llama.py — LLaMA 注意力层 Ulysses SP 适配" -- "Ulysses SP 核心流程", step 2.
+ *   [TP]   "LLM Lab 实验手记 05：注意力张量并行" -- sections 2 and 5.
+ *
+ * Conventions shared by every entry point:
+ *   - All tensor pointers are DEVICE pointers owned by the caller; the library
+ *     allocates nothing, frees nothing and keeps no mutable global state.
+ *   - Tensors are dense and row-major with head_dim innermost.  Element type is
+ *     selected by `dt`: RCGQA_BF16 (bfloat16 storage, fp32 arithmetic) or
+ *     RCGQA_FP32.
+ *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
+ *     stream).  Nothing synchronises inside the library.
+ *   - Errors: every argument that can be checked on the host is checked before
+ *     any launch; a bad one returns RCGQA_EINVAL and launches nothing.  A shape
+ *     the kernels do not implement returns RCGQA_EUNSUPPORTED.  A failed launch
+ *     returns RCGQA_EHIP.  Device-resident values (positions, kv_lens) are not
+ *     read on the host; the kernels clamp them as documented per call.
+ *   - Sizes are int; the element count of every tensor must fit in int64 and
+ *     B*S (and B*Hq) must fit in int32.
+ */
+#ifndef RCGQA_H
+#define RCGQA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  RCGQA_OK = 0,
+  RCGQA_EINVAL = 1,       /* bad argument (checked on the host, nothing launched) */
+  RCGQA_EUNSUPPORTED = 2, /* valid, but no kernel for this head_dim / dtype       */
+  RCGQA_EHIP = 3          /* the HIP runtime reported an error at launch          */
+} rcgqa_status;
+
+typedef enum { RCGQA_BF16 = 0, RCGQA_FP32 = 1 } rcgqa_dtype;
+
+/* A hipStream_t passed as an opaque pointer; NULL selects the null stream. */
+typedef void* rcgqa_stream;
+
+/*
+ * rope_apply -- rotate queries and keys in place by their positions.
+ *
+ * Defines: [L2] "Rotary Position Encoding" (RoFormer rotation; applied to Q
+ * and K only, after projection, never to V); [HF] section 2 step 3
+ * (apply_rotary_pos_emb with cos/sin from rope_theta and position_ids);
+ * [L2X] section 6.1 (linear rope_scaling factor).
+ *
+ *   pair i of every head vector, i in [0, head_dim/2), is (x[i], x[i+head_dim/2])
+ *   angle = (pos / linear_factor) * theta^(-2 i / head_dim)
+ *   (x1, x2) <- (x1 cos(angle) - x2 sin(angle), x2 cos(angle) + x1 sin(angle))
+ *
+ * q            [B, S, Hq,  head_dim]  in/out
+ * k            [B, S, Hkv, head_dim]  in/out
+ * position_ids [B, S] int32 device array, or NULL for 0..S-1 in every sequence.
+ *              Any int32 value is accepted (negative positions rotate backwards).
+ * theta        RoPE base (> 0, finite), e.g. 10000.
+ * linear_factor positions are divided by it (> 0, finite); 1 = no scaling.
+ * head_dim     even, 2..256.
+ * Angles are formed in fp64 and their cos/sin rounded to fp32; the rotation is
+ * computed in fp32 and, for bf16, rounded once to bf16 (nearest even).
+ */
+rcgqa_status rope_apply(void* q, void* k, const int32_t* position_ids,
+                        int B, int S, int Hq, int Hkv, int head_dim,
+                        float theta, float linear_factor,
+                        rcgqa_dtype dt, rcgqa_stream stream);
+
+/*
+ * attn_prefill -- full-sequence scaled-dot-product attention, grouped-query.
+ *
+ * Defines: [HF] section 1.2 steps 2-4 and section 2 steps 4-5 (scores
+ * Q K^T * scale, additive causal mask, fp32 softmax, weights @ V); the
+ * grouped-query head map of repeat_kv ([HF] section 2 step 4; [L2] GQA;
+ * [L2X] section 2.1): query head h reads K/V head h / (Hq/Hkv).
+ *
+ *   out[b,i,h,:] = sum_j softmax_j(scale * q[b,i,h,:].k[b,j,h/G,:] + mask_ij) v[b,j,h/G,:]
+ *   mask_ij = -inf where causal and j > i, else 0.
+ *
+ * q   [B, S, Hq,  head_dim]
+ * k,v [B, S, Hkv, head_dim]
+ * out [B, S, Hq,  head_dim]  (= [B, S, Hq*head_dim], the merged-heads layout)
+ * causal  0 or 1.   scale > 0, finite (usually 1/sqrt(head_dim)).
+ * Hq % Hkv == 0.  head_dim: 64 or 128 (bf16 and fp32).
+ * Scores and softmax state are fp32; for bf16 the softmax weights are rounded
+ * to bf16 as the P@V operand, accumulation is fp32 and out is rounded to bf16.
+ * out must not alias q, k or v.
+ */
+rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out,
+                          int B, int S, int Hq, int Hkv, int head_dim,
+                          int causal, float scale,
+                          rcgqa_dtype dt, rcgqa_stream stream);
+
+/*
+ * attn_decode_workspace_bytes -- bytes of scratch attn_decode needs for these
+ * sizes (partial softmax states of the split-K pass).  Pure host function.
+ * Returns 0 if an argument is not positive.
+ */
+size_t attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv);
+
+/*
+ * attn_decode -- one new query token per sequence against a KV cache.
+ *
+ * Defines: [L2] "KV cache" (the new token's query attends to all cached keys
+ * and itself; earlier rows are not recomputed) and "Grouped Multi-Query
+ * Attention" (one K/V stream serves the G query heads of its group);
+ * [HF] section 2 steps 3-5 (keys are cached after rotation).
+ *
+ *   out[b,h,:] = sum_{j < L_b} softmax_j(scale * q[b,h,:].K[b,h/G,j,:]) V[b,h/G,j,:]
+ *   L_b = clamp(kv_lens[b], 0, max_kv);  L_b == 0 gives a zero row.
+ *
+ * q        [B, Hq, head_dim]            (already rotated)
+ * k_cache  [B, Hkv, max_kv, head_dim]   rows 0..L_b-1 valid, already rotated
+ * v_cache  [B, Hkv, max_kv, head_dim]
+ * kv_lens  [B] int32 device array
+ * out      [B, Hq, head_dim]
+ * workspace  device buffer of at least attn_decode_workspace_bytes(B, Hq,
+ *            head_dim, max_kv) bytes, 256-byte aligned, owned by the caller;
+ *            no initial contents are required.  Concurrent calls must not
+ *            share a workspace.
+ * head_dim: 64 or 128.  Hq % Hkv == 0, Hq/Hkv <= 16.
+ * The result does not depend on the order in which partial states finish:
+ * partial states are merged in a fixed order (bitwise repeatable).
+ */
+rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache,
+                         const int32_t* kv_lens, void* out,
+                         int B, int Hq, int Hkv, int head_dim, int max_kv,
+                         float scale, rcgqa_dtype dt,
+                         void* workspace, size_t workspace_bytes,
+                         rcgqa_stream stream);
+
+/*
+ * kv_append -- write one new key row and value row per sequence into the cache.
+ *
+ * Defines: [L2] "KV cache" (K and V grow by appending the new token's row);
+ * [HF] section 2 step 3 (past_key_value.update after the rotation).
+ *
+ * k_new, v_new [B, Hkv, head_dim]; caches [B, Hkv, max_kv, head_dim];
+ * slots [B] int32 device array: row written for sequence b.  A slot outside
+ * [0, max_kv) writes nothing for that sequence.  head_dim even, <= 256.
+ */
+rcgqa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new,
+                       const int32_t* slots, int B, int Hkv, int head_dim, int max_kv,
+                       rcgqa_dtype dt, rcgqa_stream stream);
+
+/* Static, human-readable name of a status code. */
+const char* rcgqa_status_string(rcgqa_status s);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RCGQA_H */

@@ -1,0 +1,174 @@
+"""ctypes binding over librcgqa.so (the C ABI in include/rcgqa.h).
+
+Argument marshalling only: shapes and device pointers are read off torch
+tensors and handed to the library, which runs every step in its own HIP
+kernels on the caller's current stream.  There is no fallback: if the library
+is missing or a tensor is not a CUDA (HIP) tensor, the call raises.
+"""
+import ctypes
+import os
+
+LIB_NAME = "librcgqa.so"
+_HERE = os.path.dirname(os.path.abspath(__file__))
+
+OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+BF16, FP32 = 0, 1
+
+_lib = None
+
+
+class RcgqaError(RuntimeError):
+    """A non-OK status from the library (EHIP or unexpected)."""
+
+
+def lib_path():
+    return os.path.join(_HERE, LIB_NAME)
+
+
+def lib():
+    """Load librcgqa.so once; raise if it is not built."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    path = lib_path()
+    if not os.path.exists(path):
+        raise RcgqaError(f"{path} is not built; run `python -m rope_causal_gqa_amd.build` "
+                         "(or __graft_entry__.build()) first")
+    L = ctypes.CDLL(path)
+    vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    L.rope_apply.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, i32, vp]
+    L.rope_apply.restype = i32
+    L.attn_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.attn_prefill.restype = i32
+    L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.attn_decode_workspace_bytes.restype = sz
+    L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.attn_decode.restype = i32
+    L.kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
+    L.kv_append.restype = i32
+    L.rcgqa_status_string.argtypes = [i32]
+    L.rcgqa_status_string.restype = ctypes.c_char_p
+    _lib = L
+    return L
+
+
+def _check(status, what):
+    if status == OK:
+        return
+    msg = lib().rcgqa_status_string(status).decode()
+    if status == EINVAL:
+        raise ValueError(f"{what}: {msg}")
+    if status == EUNSUPPORTED:
+        raise NotImplementedError(f"{what}: {msg}")
+    raise RcgqaError(f"{what}: {msg}")
+
+
+def _dtype_code(t):
+    import torch
+    if t.dtype == torch.bfloat16:
+        return BF16
+    if t.dtype == torch.float32:
+        return FP32
+    raise ValueError(f"unsupported dtype {t.dtype} (bfloat16 or float32)")
+
+
+def _dev(t, name, dt=None, ndim=None):
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if ndim is not None and t.dim() != ndim:
+        raise ValueError(f"{name} must have {ndim} dims, got {tuple(t.shape)}")
+    if dt is not None and _dtype_code(t) != dt:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected the run dtype")
+    return ctypes.c_void_p(t.data_ptr())
+
+
+def _i32(t, name, n):
+    import torch
+    if t.dtype != torch.int32 or t.numel() != n:
+        raise ValueError(f"{name} must be int32 with {n} elements")
+    return _dev(t, name)
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def rope_apply(q, k, position_ids=None, theta=10000.0, linear_factor=1.0):
+    """Rotate q [B,S,Hq,D] and k [B,S,Hkv,D] in place (see rcgqa.h)."""
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D):
+        raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
+    pos = ctypes.c_void_p(0) if position_ids is None else _i32(position_ids, "position_ids", B * S)
+    st = lib().rope_apply(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), pos, B, S, Hq, Hkv, D,
+                          float(theta), float(linear_factor), dt, _stream(q))
+    _check(st, "rope_apply")
+    return q, k
+
+
+def attn_prefill(q, k, v, out=None, causal=True, scale=None):
+    """out [B,S,Hq,D] = attention(q [B,S,Hq,D], k/v [B,S,Hkv,D]) (see rcgqa.h)."""
+    import torch
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B, S, Hq, D]")
+    scale = D ** -0.5 if scale is None else scale
+    st = lib().attn_prefill(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), _dev(v, "v", dt, 4),
+                            _dev(out, "out", dt, 4), B, S, Hq, Hkv, D, int(bool(causal)),
+                            float(scale), dt, _stream(q))
+    _check(st, "attn_prefill")
+    return out
+
+
+def attn_decode_workspace_bytes(B, Hq, head_dim, max_kv):
+    return int(lib().attn_decode_workspace_bytes(B, Hq, head_dim, max_kv))
+
+
+def attn_decode(q, k_cache, v_cache, kv_lens, out=None, scale=None, workspace=None):
+    """out [B,Hq,D] = decode attention of q [B,Hq,D] over caches [B,Hkv,max_kv,D]."""
+    import torch
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    _, Hkv, max_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, max_kv, D) or tuple(v_cache.shape) != (B, Hkv, max_kv, D):
+        raise ValueError("caches must be [B, Hkv, max_kv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B, Hq, D]")
+    need = attn_decode_workspace_bytes(B, Hq, D, max_kv)
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    scale = D ** -0.5 if scale is None else scale
+    st = lib().attn_decode(_dev(q, "q", dt, 3), _dev(k_cache, "k_cache", dt, 4),
+                           _dev(v_cache, "v_cache", dt, 4), _i32(kv_lens, "kv_lens", B),
+                           _dev(out, "out", dt, 3), B, Hq, Hkv, D, max_kv, float(scale), dt,
+                           _dev(workspace, "workspace"), wbytes, _stream(q))
+    _check(st, "attn_decode")
+    return out
+
+
+def kv_append(k_cache, v_cache, k_new, v_new, slots):
+    """Write k_new/v_new [B,Hkv,D] into row slots[b] of the caches [B,Hkv,max_kv,D]."""
+    dt = _dtype_code(k_cache)
+    B, Hkv, max_kv, D = k_cache.shape
+    if tuple(v_cache.shape) != tuple(k_cache.shape):
+        raise ValueError("v_cache must match k_cache")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new/v_new must be [B, Hkv, D]")
+    st = lib().kv_append(_dev(k_cache, "k_cache", dt, 4), _dev(v_cache, "v_cache", dt, 4),
+                         _dev(k_new, "k_new", dt, 3), _dev(v_new, "v_new", dt, 3),
+                         _i32(slots, "slots", B), B, Hkv, D, max_kv, dt, _stream(k_cache))
+    _check(st, "kv_append")
+    return k_cache, v_cache

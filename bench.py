@@ -1,0 +1,210 @@
+"""Benchmark of the RoPE + causal GQA hot path on one MI355X.
+
+One step = one pass of the whole path over one batch of synthetic input:
+  prefill  (LLaMA-7B-shaped, B=2 S=4096 Hq=Hkv=32 D=128 bf16):
+           rope_apply on Q/K in place, then causal attn_prefill;
+  decode   (B=64 Hq=64 Hkv=8 D=128 bf16, context lengths uniform in [512, 8192]):
+           rope_apply on q / k_new at position = context (linear factor 2),
+           kv_append at row = context, attn_decode over context + 1 rows.
+Decode alternates between two separately allocated caches so consecutive
+steps never find the previous step's cache in the 256 MB Infinity Cache.
+
+Prints ONE JSON line.  `value` is the prefill attention throughput in TFLOP/s
+(algorithmic flops: 4*D per unmasked query-key pair per head, over the
+attn_prefill launch time measured with HIP events on the launch stream); the
+decode figure (GB/s of K/V bytes read, each row once per GQA group) rides in
+`decode`.  `roofline` is for the prefill kernel against the bf16 dense MFMA
+peak; `decode.roofline` against HBM.  `cpu_baseline` times the float64 oracle
+on a bounded sample on the host cores.
+
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+import numpy as np
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "prefill attention TFLOP/s (% MFMA peak) + decode KV-cache GB/s (% HBM peak)"
+PEAK_BF16_TFLOPS = 2500.0   # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0      # MI355X HBM3E
+PREFILL_KERNEL_SRC = os.path.join(ROOT, "rope_causal_gqa_amd", "csrc", "prefill_bf16.hip")
+DECODE_KERNEL_SRC = os.path.join(ROOT, "rope_causal_gqa_amd", "csrc", "decode.hip")
+
+
+def _sha(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def _traffic(name, src):
+    """HBM bytes per launch from committed rocprofv3 --pmc summaries, only if they
+    were taken on the current kernel source."""
+    p = os.path.join(ROOT, "profiles", f"{name}_traffic.json")
+    if not os.path.exists(p):
+        return None
+    d = json.load(open(p))
+    if d.get("kernel_src_sha") != _sha(src):
+        return None
+    return d.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(budget_s=12.0):
+    """Time the float64 oracle on a bounded sample of the prefill workload:
+    whole (batch, head) rows of the causal S=4096 attention, RoPE included."""
+    import oracle
+    from rope_causal_gqa_amd import workloads as W
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        threads = 1
+    w = W.WORKLOADS["c3"]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    done, flops = 0, 0.0
+    t0 = time.perf_counter()
+    while done == 0 or time.perf_counter() - t0 < budget_s:
+        q = W.to_f64(W.draw(rng, (1, w.S, 1, w.D), "bf16"), "bf16")
+        k = W.to_f64(W.draw(rng, (1, w.S, 1, w.D), "bf16"), "bf16")
+        v = W.to_f64(W.draw(rng, (1, w.S, 1, w.D), "bf16"), "bf16")
+        qr, kr = oracle.rope_apply(q, k, None, w.theta, w.factor)
+        oracle.attention(qr, kr, v, True, w.scale)
+        done += 1
+        flops += 4.0 * w.D * (w.S * (w.S + 1) // 2)
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(threads), "kind": "oracle",
+            "sample": f"{done} whole (batch, head) pairs of the B=2 S=4096 D=128 causal prefill "
+                      f"(RoPE + attention, float64 numpy) in {dt:.1f} s; cpus visible "
+                      f"{len(os.sched_getaffinity(0))}"}
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
+              "(this library has no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import rope_causal_gqa_amd as R
+    from rope_causal_gqa_amd import workloads as W
+
+    R.lib()  # fail loudly if the HIP library is missing
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    # ---- prefill inputs (LLaMA-7B-shaped)
+    wp = W.WORKLOADS["c3"]
+    tb = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+    q, k, v = (tb(a) for a in W.prefill_inputs(wp))
+    out = torch.empty_like(q)
+
+    # ---- decode inputs (GQA decode, bf16 cache); the caches are drawn on the device
+    wd = W.WORKLOADS["c5"]
+    rng = np.random.Generator(np.random.PCG64(wd.seed))
+    ctx = rng.integers(wd.ctx_lo, wd.ctx_hi + 1, size=wd.B).astype(np.int32)
+    ctx_d = torch.from_numpy(ctx).to(dev)
+    lens_d = ctx_d + 1
+    pos_d = ctx_d.view(wd.B, 1).contiguous()
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(wd.seed)
+    dq = torch.randn((wd.B, 1, wd.Hq, wd.D), generator=gen, device=dev).to(torch.bfloat16)
+    dkn = torch.randn((wd.B, 1, wd.Hkv, wd.D), generator=gen, device=dev).to(torch.bfloat16)
+    dvn = torch.randn((wd.B, wd.Hkv, wd.D), generator=gen, device=dev).to(torch.bfloat16)
+    caches = []
+    for _ in range(2):
+        kc = torch.empty((wd.B, wd.Hkv, wd.max_kv, wd.D), dtype=torch.bfloat16, device=dev)
+        vc = torch.empty_like(kc)
+        for b in range(wd.B):
+            kc[b].copy_(torch.randn((wd.Hkv, wd.max_kv, wd.D), generator=gen, device=dev))
+            vc[b].copy_(torch.randn((wd.Hkv, wd.max_kv, wd.D), generator=gen, device=dev))
+        caches.append((kc, vc))
+    dout = torch.empty((wd.B, wd.Hq, wd.D), dtype=torch.bfloat16, device=dev)
+    ws = torch.empty(R.attn_decode_workspace_bytes(wd.B, wd.Hq, wd.D, wd.max_kv), dtype=torch.uint8, device=dev)
+
+    kv_bytes = float(np.sum(ctx.astype(np.int64) + 1)) * wd.Hkv * wd.D * 2 * 2
+    dec_bytes = kv_bytes + 2 * wd.B * wd.Hq * wd.D * 2          # + q read + out write
+    pre_flops = wp.flops()
+
+    stream = torch.cuda.current_stream(dev)
+    ev = lambda: torch.cuda.Event(enable_timing=True)
+
+    def step(i, rec=None):
+        kc, vc = caches[i % 2]
+        if rec: rec[0].record(stream)
+        R.rope_apply(q, k, None, wp.theta, wp.factor)
+        if rec: rec[1].record(stream)
+        R.attn_prefill(q, k, v, out, causal=True, scale=wp.scale)
+        if rec: rec[2].record(stream)
+        R.rope_apply(dq, dkn, pos_d, wd.theta, wd.factor)
+        R.kv_append(kc, vc, dkn.view(wd.B, wd.Hkv, wd.D), dvn, ctx_d)
+        if rec: rec[3].record(stream)
+        R.attn_decode(dq.view(wd.B, wd.Hq, wd.D), kc, vc, lens_d, dout, scale=wd.scale, workspace=ws)
+        if rec: rec[4].record(stream)
+
+    for i in range(args.warmup):
+        step(i)
+    torch.cuda.synchronize()
+    recs = [[ev() for _ in range(5)] for _ in range(args.steps)]
+    t_start, t_end = ev(), ev()
+    torch.cuda.synchronize()
+    t_start.record(stream)
+    for i in range(args.steps):
+        step(i, recs[i])
+    t_end.record(stream)
+    torch.cuda.synchronize()
+    total_ms = t_start.elapsed_time(t_end)
+    rope_ms = np.array([r[0].elapsed_time(r[1]) for r in recs])
+    pre_ms = np.array([r[1].elapsed_time(r[2]) for r in recs])
+    dec_ms = np.array([r[3].elapsed_time(r[4]) for r in recs])
+
+    pre_tflops = pre_flops / (pre_ms.mean() * 1e-3) / 1e12
+    dec_gbps = dec_bytes / (dec_ms.mean() * 1e-3) / 1e9
+    rope_bytes = 2.0 * wp.B * wp.S * (wp.Hq + wp.Hkv) * wp.D * 2
+    res = {
+        "metric": METRIC,
+        "value": round(pre_tflops, 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(total_ms / args.steps, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "LLaMA-7B-shaped causal MHA prefill B=2 S=4096 Hq=Hkv=32 D=128 + "
+                               "GQA decode B=64 Hq=64 Hkv=8 D=128 ctx~U[512,8192]",
+                   "global_batch": wp.B, "seq_len": wp.S, "parallelism": "single-gpu"},
+        "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
+                     "traffic": _traffic("prefill_c3", PREFILL_KERNEL_SRC),
+                     "kernel": "prefill_bf16_kernel<128>", "launch_ms": round(float(pre_ms.mean()), 4)},
+        "decode": {"metric": "decode KV-cache GB/s", "value": round(dec_gbps, 1), "unit": "GB/s",
+                   "launch_ms": round(float(dec_ms.mean()), 4),
+                   "algorithmic_bytes": dec_bytes,
+                   "roofline": {"bound": "hbm", "achieved": round(dec_gbps, 1), "peak": PEAK_HBM_GBPS,
+                                "unit": "GB/s", "frac": round(dec_gbps / PEAK_HBM_GBPS, 4),
+                                "traffic": _traffic("decode_c5", DECODE_KERNEL_SRC)}},
+        "rope": {"value": round(rope_bytes / (rope_ms.mean() * 1e-3) / 1e9, 1), "unit": "GB/s",
+                 "launch_ms": round(float(rope_ms.mean()), 4)},
+        "cpu_baseline": None,
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

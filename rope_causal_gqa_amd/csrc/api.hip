@@ -1,0 +1,105 @@
+// C ABI of librcgqa (declared in include/rcgqa.h): host-side validation and
+// dispatch to the gfx950 kernels.  Nothing here allocates, synchronises or
+// keeps state; every check that can be made on the host is made before the
+// first launch, so a rejected call launches nothing.
+#include <cmath>
+#include <cstdint>
+
+#include "launch.h"
+#include "rcgqa.h"
+
+namespace {
+
+constexpr int64_t kI32Max = 2147483647;
+
+bool pos_int(int x) { return x >= 1; }
+bool good_dtype(rcgqa_dtype dt) { return dt == RCGQA_BF16 || dt == RCGQA_FP32; }
+bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+
+// Product of positive ints, or -1 on int64 overflow.
+int64_t mul(std::initializer_list<int64_t> xs) {
+  int64_t p = 1;
+  for (int64_t x : xs) {
+    if (x <= 0) return -1;
+    if (p > INT64_MAX / x) return -1;
+    p *= x;
+  }
+  return p;
+}
+
+bool attn_head_dim(int d) { return d == 64 || d == 128; }
+
+rcgqa_status hip_status(hipError_t e) { return e == hipSuccess ? RCGQA_OK : RCGQA_EHIP; }
+
+}  // namespace
+
+extern "C" {
+
+const char* rcgqa_status_string(rcgqa_status s) {
+  switch (s) {
+    case RCGQA_OK: return "ok";
+    case RCGQA_EINVAL: return "invalid argument";
+    case RCGQA_EUNSUPPORTED: return "unsupported head_dim or dtype";
+    case RCGQA_EHIP: return "HIP runtime error at launch";
+  }
+  return "unknown status";
+}
+
+rcgqa_status rope_apply(void* q, void* k, const int32_t* position_ids, int B, int S, int Hq, int Hkv,
+                        int head_dim, float theta, float linear_factor, rcgqa_dtype dt, rcgqa_stream stream) {
+  if (!q || !k || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2) return RCGQA_EINVAL;
+  if (!finite_pos(theta) || !finite_pos(linear_factor)) return RCGQA_EINVAL;
+  const int64_t tokens = mul({B, S});
+  if (tokens < 0 || tokens > kI32Max || mul({tokens, Hq, head_dim}) < 0) return RCGQA_EINVAL;
+  if (head_dim > 256) return RCGQA_EUNSUPPORTED;
+  return hip_status(rcgqa::launch_rope(q, k, position_ids, B, S, Hq, Hkv, head_dim, (double)theta,
+                                       (double)linear_factor, dt == RCGQA_BF16, (hipStream_t)stream));
+}
+
+rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq, int Hkv,
+                          int head_dim, int causal, float scale, rcgqa_dtype dt, rcgqa_stream stream) {
+  if (!q || !k || !v || !out || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (out == q || out == k || out == v) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0) return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || (S + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  if (dt == RCGQA_BF16)
+    return hip_status(rcgqa::launch_prefill_bf16(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, st));
+  return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, B, S,
+                                              Hq, Hkv, head_dim, causal != 0, scale, st));
+}
+
+size_t attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv) {
+  if (!pos_int(B) || !pos_int(Hq) || !pos_int(head_dim) || !pos_int(max_kv)) return 0;
+  return rcgqa::decode_workspace_bytes(B, Hq, head_dim, max_kv);
+}
+
+rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_lens,
+                         void* out, int B, int Hq, int Hkv, int head_dim, int max_kv, float scale,
+                         rcgqa_dtype dt, void* workspace, size_t workspace_bytes, rcgqa_stream stream) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !out || !workspace || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (B > 65535 || Hq > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || Hq / Hkv > 16) return RCGQA_EUNSUPPORTED;
+  if (workspace_bytes < rcgqa::decode_workspace_bytes(B, Hq, head_dim, max_kv)) return RCGQA_EINVAL;
+  return hip_status(rcgqa::launch_decode(q, k_cache, v_cache, kv_lens, out, B, Hq, Hkv, head_dim, max_kv, scale,
+                                         dt == RCGQA_BF16, workspace, (hipStream_t)stream));
+}
+
+rcgqa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* slots,
+                       int B, int Hkv, int head_dim, int max_kv, rcgqa_dtype dt, rcgqa_stream stream) {
+  if (!k_cache || !v_cache || !k_new || !v_new || !slots || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(Hkv) || !pos_int(max_kv) || head_dim < 2 || head_dim % 2) return RCGQA_EINVAL;
+  if (B > 65535 || Hkv > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
+  if (head_dim > 256) return RCGQA_EUNSUPPORTED;
+  return hip_status(rcgqa::launch_kv_append(k_cache, v_cache, k_new, v_new, slots, B, Hkv, head_dim, max_kv,
+                                            dt == RCGQA_BF16, (hipStream_t)stream));
+}
+
+}  // extern "C"

@@ -1,0 +1,196 @@
+// bf16 prefill attention on CDNA4 matrix cores (gfx950).
+//
+// Method: "【HuggingFace Transformers】LlamaAttention源码解析", section 1.2 steps 2-4
+// and section 2 steps 4-5: scores = scale * Q K^T, additive causal mask,
+// softmax kept in fp32 (also "Llama2 Transformer架构解析与优化实践" section 3.2),
+// weights @ V; query head h reads K/V head h / G (repeat_kv).
+//
+// Design (one workgroup = 4 waves = 128 query rows of one (batch, head)):
+//  * K/V tiles of 64 keys are staged in LDS with an XOR swizzle of 16-byte
+//    chunks (chunk ^ row) so both read patterns below are bank-conflict free.
+//  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
+//    K rows are the A operand (read straight from LDS), the wave's 32 query
+//    rows are the B operand (held in registers for the whole kernel).  In the
+//    output layout every lane then owns ONE query row (lane % 32) and 32 of
+//    the tile's 64 keys; the other 32 sit in lane ^ 32, so row max / row sum
+//    need one v_permlane32_swap and no LDS.
+//  * Online softmax in the exp2 domain with fp32 running max / sum per lane.
+//  * O^T = V^T P^T, again 32x32x16: P^T comes straight from the score
+//    registers (converted to bf16; the MFMA's k index is permuted to match the
+//    score layout), V^T is read from the row-major V tile with the gfx950 LDS
+//    transpose read (ds_read_b64_tr_b16).  O^T keeps the query row on the lane,
+//    so the rescale by exp2(m_old - m_new) is one multiply per accumulator.
+//  * Causal: tiles past the block's last row are never loaded; a wave skips
+//    the math of tiles past its own last row; only diagonal / tail tiles pay
+//    for per-element masking.  Heaviest query tiles are dispatched first.
+#include "common.h"
+#include "launch.h"
+
+namespace rcgqa {
+
+namespace {
+constexpr int BM = 128;  // query rows per workgroup (32 per wave)
+constexpr int BN = 64;   // keys per K/V tile
+constexpr int NT = 256;  // threads per workgroup
+}  // namespace
+
+template <int D>
+__global__ __launch_bounds__(NT) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                          const bf16* __restrict__ v, bf16* __restrict__ out,
+                                                          int S, int Hq, int Hkv, int causal, float c_log2) {
+  constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
+  constexpr int DB = D / 32;  // 32-wide blocks of the output head dim
+  constexpr int CH = D / 8;   // 16-byte chunks per row
+  constexpr int SW = CH - 1;  // swizzle mask
+  static_assert(CH <= 16 && (CH & (CH - 1)) == 0, "D must be 64 or 128");
+  __shared__ __attribute__((aligned(16))) bf16 sk[BN * D];
+  __shared__ __attribute__((aligned(16))) bf16 sv[BN * D];
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int col = lane & 31, hf = lane >> 5;
+  const int bh = blockIdx.x, b = bh / Hq, h = bh - b * Hq;
+  const int kvh = h / (Hq / Hkv);
+  const int q0 = ((int)gridDim.y - 1 - (int)blockIdx.y) * BM;  // heaviest tiles first
+  const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
+  const bf16* kb = k + (size_t)b * S * kvrs + (size_t)kvh * D;
+  const bf16* vb = v + (size_t)b * S * kvrs + (size_t)kvh * D;
+
+  const int qrow = q0 + w * 32 + col;  // this lane's query row
+  bf16x8 qf[KS];
+  if (qrow < S) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)b * S + qrow) * qrs + (size_t)h * D);
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) qf[ks] = src[2 * ks + hf];
+  } else {
+#pragma unroll
+    for (int ks = 0; ks < KS; ks++) qf[ks] = bf16x8{};
+  }
+
+  f32x16 o[DB];
+#pragma unroll
+  for (int db = 0; db < DB; db++) o[db] = f32x16{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  const int kv_end = causal ? min(S, q0 + BM) : S;
+  const int ntiles = (kv_end + BN - 1) / BN;
+  const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
+
+  // transpose-read addressing of V (fixed per lane)
+  const int r16 = lane & 15, g = lane >> 4;
+  const int vrow_base = 4 * hf + (r16 >> 2);
+  const int vcol_base = 16 * (g & 1) + 4 * (r16 & 3);
+
+  for (int t = 0; t < ntiles; t++) {
+    const int kv0 = t * BN;
+    __syncthreads();  // previous tile fully consumed
+    for (int idx = tid; idx < BN * CH; idx += NT) {
+      const int r = idx / CH, c = idx - r * CH, key = kv0 + r;
+      bf16x8 kk{}, vv{};
+      if (key < S) {
+        kk = reinterpret_cast<const bf16x8*>(kb + (size_t)key * kvrs)[c];
+        vv = reinterpret_cast<const bf16x8*>(vb + (size_t)key * kvrs)[c];
+      }
+      const int off = r * D + ((c ^ (r & SW)) << 3);
+      *reinterpret_cast<bf16x8*>(sk + off) = kk;
+      *reinterpret_cast<bf16x8*>(sv + off) = vv;
+    }
+    __syncthreads();
+    if (causal && kv0 > wrow_hi) continue;  // whole tile masked for this wave
+
+    // S^T = K Q^T: two 32-key blocks
+    f32x16 s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; kb2++) {
+      s[kb2] = f32x16{};
+      const int r = kb2 * 32 + col;
+#pragma unroll
+      for (int ks = 0; ks < KS; ks++) {
+        const int c = 2 * ks + hf;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (r & SW)) << 3));
+        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
+      }
+    }
+
+    // scale into the log2 domain, mask, row max
+    const bool need_mask = (causal && kv0 + BN - 1 > wrow_lo) || (kv0 + BN > S);
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; kb2++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        float x = s[kb2][i] * c_log2;
+        if (need_mask) {
+          const int key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+          if (key >= S || (causal && key > qrow)) x = -INFINITY;
+        }
+        s[kb2][i] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = half_swap_max(mx);
+    const float m_new = fmaxf(m_run, mx);
+    const float m_base = (m_new == -INFINITY) ? 0.f : m_new;
+    const float alpha = fast_exp2(m_run - m_base);
+    float psum = 0.f;
+    bf16x8 pf[4];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; kb2++) {
+#pragma unroll
+      for (int i = 0; i < 16; i++) {
+        const float p = fast_exp2(s[kb2][i] - m_base);
+        psum += p;
+        pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DB; db++) o[db] *= alpha;
+
+    // O^T += V^T P^T over four 16-key chunks
+#pragma unroll
+    for (int kc = 0; kc < 4; kc++) {
+      const int row1 = 16 * kc + vrow_base, row2 = row1 + 8;
+#pragma unroll
+      for (int db = 0; db < DB; db++) {
+        const int cc = 32 * db + vcol_base;
+        const bf16* p1 = sv + row1 * D + ((((cc >> 3) ^ (row1 & SW))) << 3) + (cc & 7);
+        const bf16* p2 = sv + row2 * D + ((((cc >> 3) ^ (row2 & SW))) << 3) + (cc & 7);
+        const bf16x8 a = cat8(lds_read_tr16(p1), lds_read_tr16(p2));
+        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
+      }
+    }
+  }
+
+  const float l_tot = half_swap_sum(l_run);
+  const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
+  if (qrow < S) {
+    bf16* dst = out + ((size_t)b * S + qrow) * qrs + (size_t)h * D;
+#pragma unroll
+    for (int db = 0; db < DB; db++) {
+#pragma unroll
+      for (int a = 0; a < 4; a++) {
+        const int d = 32 * db + 8 * a + 4 * hf;
+        bf16x4 y;
+#pragma unroll
+        for (int c = 0; c < 4; c++) y[c] = (bf16)(o[db][4 * a + c] * inv);
+        *reinterpret_cast<bf16x4*>(dst + d) = y;
+      }
+    }
+  }
+}
+
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
+                               int Hkv, int D, bool causal, float scale, hipStream_t st) {
+  const dim3 grid((unsigned)(B * Hq), (unsigned)((S + BM - 1) / BM)), block(NT);
+  const float c_log2 = (float)((double)scale * 1.4426950408889634);
+  if (D == 64)
+    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2);
+  else
+    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2);
+  return hipGetLastError();
+}
+
+}  // namespace rcgqa

@@ -1,0 +1,126 @@
+"""The C-ABI library loads and exports what include/rcgqa.h declares; host-side
+argument checks reject bad calls before any launch (CPU only: no call here
+passes validation, so nothing reaches the GPU)."""
+import ctypes
+import os
+import re
+
+import pytest
+
+import rope_causal_gqa_amd as R
+from rope_causal_gqa_amd import _binding as BD
+
+HEADER = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "include", "rcgqa.h")
+
+pytestmark = pytest.mark.skipif(not os.path.exists(R.lib_path()), reason="librcgqa.so not built")
+
+
+def _declared():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b([a-z_][a-z0-9_]*)\s*\(", src)) - {"if", "sizeof"})
+
+
+def test_exports_every_declared_symbol():
+    names = _declared()
+    assert set(names) >= {"rope_apply", "attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
+                          "kv_append", "rcgqa_status_string"}
+    L = R.lib()
+    for n in names:
+        assert hasattr(L, n), n
+    out = os.popen(f"nm -D --defined-only {R.lib_path()}").read()
+    for n in names:
+        assert re.search(rf"\sT {n}$", out, re.M), n
+
+
+def test_status_strings():
+    L = R.lib()
+    assert L.rcgqa_status_string(0) == b"ok"
+    assert L.rcgqa_status_string(1) == b"invalid argument"
+    assert L.rcgqa_status_string(2).startswith(b"unsupported")
+    assert L.rcgqa_status_string(3).startswith(b"HIP")
+    assert L.rcgqa_status_string(99) == b"unknown status"
+
+
+def test_workspace_bytes():
+    L = R.lib()
+    a = L.attn_decode_workspace_bytes(64, 64, 128, 8193)
+    assert a >= 64 * 64 * 130 * 4                  # at least one partial state per row
+    assert L.attn_decode_workspace_bytes(64, 64, 128, 16386) >= a
+    assert L.attn_decode_workspace_bytes(0, 64, 128, 10) == 0
+    assert L.attn_decode_workspace_bytes(1, 1, 128, -1) == 0
+
+
+FAKE = ctypes.c_void_p(4096)   # never dereferenced: every call below fails validation
+
+
+@pytest.mark.parametrize("args", [
+    dict(q=None),
+    dict(B=0), dict(S=0), dict(Hq=0), dict(Hkv=0), dict(Hq=6, Hkv=4),
+    dict(D=63), dict(D=0), dict(theta=0.0), dict(theta=float("inf")), dict(factor=0.0),
+    dict(factor=float("nan")), dict(dt=7),
+])
+def test_rope_rejects(args):
+    a = dict(q=FAKE, k=FAKE, B=1, S=4, Hq=8, Hkv=2, D=64, theta=1e4, factor=1.0, dt=0)
+    a.update(args)
+    st = R.lib().rope_apply(a["q"], a["k"], None, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["theta"],
+                            a["factor"], a["dt"], None)
+    assert st == BD.EINVAL
+
+
+def test_rope_unsupported_head_dim():
+    assert R.lib().rope_apply(FAKE, FAKE, None, 1, 1, 1, 1, 258, 1e4, 1.0, 0, None) == BD.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("args", [
+    dict(out=None), dict(same=True), dict(B=-1), dict(Hq=3, Hkv=2), dict(causal=2), dict(scale=0.0),
+    dict(scale=float("nan")), dict(D=7),
+])
+def test_prefill_rejects(args):
+    a = dict(q=FAKE, out=ctypes.c_void_p(8192), B=1, S=4, Hq=8, Hkv=2, D=64, causal=1, scale=0.125, dt=0)
+    a.update(args)
+    out = a["q"] if a.get("same") else a["out"]
+    st = R.lib().attn_prefill(a["q"], FAKE, FAKE, out, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["causal"],
+                              a["scale"], a["dt"], None)
+    assert st == BD.EINVAL
+
+
+@pytest.mark.parametrize("D", [32, 96, 256])
+def test_prefill_unsupported_head_dim(D):
+    assert R.lib().attn_prefill(FAKE, FAKE, FAKE, ctypes.c_void_p(8192), 1, 4, 8, 2, D, 1, 0.1, 0, None) \
+        == BD.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("args", [
+    dict(ws=None), dict(wbytes=0), dict(ws_addr=4096 + 8), dict(Hq=12, Hkv=8), dict(max_kv=0), dict(scale=-1.0),
+    dict(lens=None),
+])
+def test_decode_rejects(args):
+    a = dict(B=2, Hq=8, Hkv=2, D=128, max_kv=300, scale=0.1, ws_addr=4096 * 16, wbytes=1 << 30, lens=FAKE)
+    a.update(args)
+    ws = None if "ws" in args else ctypes.c_void_p(a["ws_addr"])
+    st = R.lib().attn_decode(FAKE, FAKE, FAKE, a["lens"], ctypes.c_void_p(8192), a["B"], a["Hq"], a["Hkv"], a["D"],
+                             a["max_kv"], a["scale"], 0, ws, a["wbytes"], None)
+    assert st == BD.EINVAL
+
+
+def test_decode_unsupported_group():
+    st = R.lib().attn_decode(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(8192), 1, 32, 1, 128, 10, 0.1, 0,
+                             ctypes.c_void_p(4096 * 16), 1 << 30, None)
+    assert st == BD.EUNSUPPORTED
+
+
+def test_kv_append_rejects():
+    L = R.lib()
+    assert L.kv_append(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 4, 0, None) == BD.EINVAL
+    assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 63, 4, 0, None) == BD.EINVAL
+    assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 0, 0, None) == BD.EINVAL
+
+
+def test_binding_requires_device_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):
+        R.rope_apply(q, q.clone())
+    with pytest.raises(ValueError):
+        R.attn_prefill(q, q, q)

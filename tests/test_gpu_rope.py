@@ -1,0 +1,62 @@
+"""rope_apply on the GPU against the float64 oracle."""
+import numpy as np
+import pytest
+
+import oracle
+import rope_causal_gqa_amd as R
+from rope_causal_gqa_amd import workloads as W
+from tests.gpu_helpers import announce, check, dev, host64
+
+pytestmark = pytest.mark.gpu
+
+
+def _run(q, k, pos, theta, factor, dtype, what):
+    import torch
+    announce(what)
+    qd, kd = dev(q, dtype), dev(k, dtype)
+    pd = None if pos is None else torch.from_numpy(np.ascontiguousarray(pos, dtype=np.int32)).cuda()
+    R.rope_apply(qd, kd, pd, theta, factor)
+    torch.cuda.synchronize()
+    qr, kr = oracle.rope_apply(W.to_f64(q, dtype), W.to_f64(k, dtype), pos, theta, factor)
+    check(host64(qd), qr, dtype, what + " q")
+    check(host64(kd), kr, dtype, what + " k")
+
+
+@pytest.mark.parametrize("name", ["c1", "c2b"])
+def test_rope_workloads(name):
+    w = W.WORKLOADS[name]
+    q, k, _ = W.prefill_inputs(w)
+    _run(q, k, None, w.theta, w.factor, w.dtype, f"rope {name}")
+
+
+def test_rope_decode_positions_linear_factor():
+    w = W.WORKLOADS["c5"]
+    rng = np.random.Generator(np.random.PCG64(w.seed))
+    ctx = rng.integers(w.ctx_lo, w.ctx_hi + 1, size=w.B).astype(np.int32)
+    q = W.draw(rng, (w.B, 1, w.Hq, w.D), "bf16")
+    k = W.draw(rng, (w.B, 1, w.Hkv, w.D), "bf16")
+    _run(q, k, ctx.reshape(w.B, 1), w.theta, w.factor, "bf16", "rope c5 q/k_new at ctx, factor 2")
+
+
+def test_rope_c3_full_size():
+    w = W.WORKLOADS["c3"]
+    q, k, _ = W.prefill_inputs(w)
+    _run(q, k, None, w.theta, w.factor, "bf16", "rope c3 full")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [2, 6, 64, 128, 256])
+def test_rope_head_dims(dtype, D):
+    B, S, Hq, Hkv = 2, 33, 4, 2
+    q = W.random_case(D, (B, S, Hq, D), dtype)
+    k = W.random_case(D + 1, (B, S, Hkv, D), dtype)
+    pos = np.random.Generator(np.random.PCG64(D)).integers(-50, 9000, size=(B, S)).astype(np.int32)
+    _run(q, k, pos, 500000.0, 4.0, dtype, f"rope D={D} {dtype} random positions")
+
+
+def test_rope_fp32_long_positions():
+    # the fp32 bound must hold far from position 0 as well
+    q = W.random_case(5, (1, 8, 2, 128), "fp32")
+    k = W.random_case(6, (1, 8, 1, 128), "fp32")
+    pos = np.array([[0, 1, 127, 4095, 8192, 65535, 1 << 20, 2_000_000_000]], dtype=np.int32)
+    _run(q, k, pos, 10000.0, 1.0, "fp32", "rope fp32 long positions")

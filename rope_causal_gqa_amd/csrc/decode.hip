@@ -113,6 +113,222 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   out[((size_t)b * Hq + h) * D + d] = (T)(n > 0 ? num / den : 0.f);
 }
 
+// Pass 1, bf16 form, on matrix cores.  One workgroup = 4 waves handles one
+// split of KCH keys of one (batch, KV head) for all G <= 16 query heads of the
+// group, so each K/V row is read from HBM once per group.  Each wave streams
+// its own 32-key tiles (tiles w, w+4, ... of the split) through a private LDS
+// region, with the next tile prefetched into registers while the current one
+// is computed; waves never wait for each other until the final combine.
+//   S^T (32 keys x 16 heads) = K Q^T   v_mfma_f32_16x16x32_bf16, K from LDS
+//   O^T (D x 16 heads)      += V^T P^T  same MFMA, V^T via the LDS transpose read
+// In both outputs a lane owns one head (lane % 16), so the online-softmax
+// rescale is one multiply per accumulator.  The 4 waves' states are combined
+// in LDS and written as one partial state per (split, head).
+namespace {
+constexpr int KCH = 512;   // keys per split
+constexpr int TK = 32;     // keys per wave tile
+constexpr int DW = 4;      // waves per workgroup
+}
+
+template <int D>
+__global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __restrict__ q,
+                                                             const bf16* __restrict__ kc,
+                                                             const bf16* __restrict__ vc,
+                                                             const int32_t* __restrict__ kv_lens,
+                                                             float* __restrict__ ws, int Hq, int Hkv, int max_kv,
+                                                             int nsplit, float c_log2) {
+  constexpr int CH = D / 8;         // 16-byte chunks per row
+  constexpr int SW = CH - 1;        // swizzle mask
+  constexpr int KSTEP = D / 32;     // k-steps of Q K^T
+  constexpr int DBLK = D / 16;      // 16-wide output blocks
+  constexpr int LD_PER_LANE = TK * CH / 64;  // 16-byte loads per lane per tile (K or V)
+  constexpr int WAVE_LDS = 2 * TK * D;       // bf16 elements per wave (K + V tile)
+  __shared__ __attribute__((aligned(16))) bf16 lds[DW * WAVE_LDS];
+
+  const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
+  const int L = min(max(kv_lens[b], 0), max_kv);
+  const int k0 = split * KCH;
+  if (k0 >= L) return;  // uniform: nothing in this split
+  const int kend = min(L, k0 + KCH);
+  const int ntile = (kend - k0 + TK - 1) / TK;
+  const int G = Hq / Hkv;
+
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int n = lane & 15, g = lane >> 4;  // head column / lane group of the 16x16 layouts
+  bf16* sk = lds + w * WAVE_LDS;
+  bf16* sv = sk + TK * D;
+  const size_t head_base = ((size_t)b * Hkv + kvh) * (size_t)max_kv * D;
+  const bf16* kb = kc + head_base;
+  const bf16* vb = vc + head_base;
+
+  // Q^T operand: lane holds q[head n][32 ks + 8 g .. +7]; heads >= G are zero
+  bf16x8 qf[KSTEP];
+  {
+    const bool hv = n < G;
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)b * Hq + kvh * G + (hv ? n : 0)) * D);
+#pragma unroll
+    for (int ks = 0; ks < KSTEP; ks++) qf[ks] = hv ? src[4 * ks + g] : bf16x8{};
+  }
+
+  f32x4 o[DBLK];
+#pragma unroll
+  for (int i = 0; i < DBLK; i++) o[i] = f32x4{};
+  float m_run = -INFINITY, l_run = 0.f;
+
+  // register prefetch of one tile: lane loads chunk (lane % CH) of rows lane / CH + (64 / CH) * p
+  bf16x8 pk[LD_PER_LANE], pv[LD_PER_LANE];
+  auto load_tile = [&](int t) {
+    const int t0 = k0 + t * TK;
+#pragma unroll
+    for (int p = 0; p < LD_PER_LANE; p++) {
+      const int idx = p * 64 + lane, r = idx / CH, c = idx - r * CH;
+      const int key = t0 + r;
+      if (key < kend) {
+        pk[p] = reinterpret_cast<const bf16x8*>(kb + (size_t)key * D)[c];
+        pv[p] = reinterpret_cast<const bf16x8*>(vb + (size_t)key * D)[c];
+      } else {
+        pk[p] = bf16x8{};
+        pv[p] = bf16x8{};
+      }
+    }
+  };
+  auto store_tile = [&]() {
+#pragma unroll
+    for (int p = 0; p < LD_PER_LANE; p++) {
+      const int idx = p * 64 + lane, r = idx / CH, c = idx - r * CH;
+      const int off = r * D + ((c ^ (r & SW)) << 3);
+      *reinterpret_cast<bf16x8*>(sk + off) = pk[p];
+      *reinterpret_cast<bf16x8*>(sv + off) = pv[p];
+    }
+  };
+
+  // V transpose-read addressing (fixed per lane): rows 4g + r/4 (+16), cols 16 db + 4 (r % 4)
+  const int r16 = lane & 15;
+  const int vr1 = 4 * g + (r16 >> 2), vr2 = vr1 + 16;
+  const int vcb = 4 * (r16 & 3);
+
+  int t = w;
+  if (t < ntile) load_tile(t);
+  for (; t < ntile; t += DW) {
+    __builtin_amdgcn_wave_barrier();
+    store_tile();
+    __builtin_amdgcn_wave_barrier();
+    if (t + DW < ntile) load_tile(t + DW);
+    const int t0 = k0 + t * TK;
+
+    f32x4 s[2];
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; kb2++) {
+      s[kb2] = f32x4{};
+      const int r = 16 * kb2 + n;
+#pragma unroll
+      for (int ks = 0; ks < KSTEP; ks++) {
+        const int c = 4 * ks + g;
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (r & SW)) << 3));
+        s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[kb2], 0, 0, 0);
+      }
+    }
+    // lane holds keys t0 + 16 kb2 + 4 g + j for head n
+    float mx = -INFINITY;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; kb2++) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        float x = s[kb2][j] * c_log2;
+        if (t0 + 16 * kb2 + 4 * g + j >= kend) x = -INFINITY;
+        s[kb2][j] = x;
+        mx = fmaxf(mx, x);
+      }
+    }
+    mx = fmaxf(mx, __shfl_xor(mx, 16));
+    mx = half_swap_max(mx);
+    const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid key
+    const float alpha = fast_exp2(m_run - m_new);
+    bf16x8 pf;
+    float psum = 0.f;
+#pragma unroll
+    for (int kb2 = 0; kb2 < 2; kb2++) {
+#pragma unroll
+      for (int j = 0; j < 4; j++) {
+        const float p = fast_exp2(s[kb2][j] - m_new);
+        psum += p;
+        pf[4 * kb2 + j] = (bf16)p;
+      }
+    }
+    l_run = l_run * alpha + psum;
+    m_run = m_new;
+#pragma unroll
+    for (int db = 0; db < DBLK; db++) {
+      o[db] *= alpha;
+      const int cc = 16 * db + vcb;
+      const bf16* p1 = sv + vr1 * D + (((cc >> 3) ^ (vr1 & SW)) << 3) + (cc & 7);
+      const bf16* p2 = sv + vr2 * D + (((cc >> 3) ^ (vr2 & SW)) << 3) + (cc & 7);
+      const bf16x8 a = cat8(lds_read_tr16(p1), lds_read_tr16(p2));
+      o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, o[db], 0, 0, 0);
+    }
+  }
+
+  // per-wave state of head n: m_run (same in all 4 lane groups), l summed over groups
+  l_run += __shfl_xor(l_run, 16);
+  l_run = half_swap_sum(l_run);
+
+  // combine the waves in LDS: [w][16 heads][D + 2] fp32
+  __syncthreads();
+  float* st = reinterpret_cast<float*>(lds);
+  constexpr int SR = D + 2;
+  float* mine = st + (w * 16 + n) * SR;
+  if (g == 0) {
+    mine[0] = m_run;
+    mine[1] = l_run;
+  }
+#pragma unroll
+  for (int db = 0; db < DBLK; db++)
+#pragma unroll
+    for (int j = 0; j < 4; j++) mine[2 + 16 * db + 4 * g + j] = o[db][j];
+  __syncthreads();
+  for (int idx = tid; idx < G * D; idx += 64 * DW) {
+    const int hh = idx / D, d = idx - hh * D;
+    float M = -INFINITY;
+#pragma unroll
+    for (int ww = 0; ww < DW; ww++) M = fmaxf(M, st[(ww * 16 + hh) * SR]);
+    float num = 0.f, den = 0.f;
+#pragma unroll
+    for (int ww = 0; ww < DW; ww++) {
+      const float* sw = st + (ww * 16 + hh) * SR;
+      const float e = sw[1] > 0.f ? fast_exp2(sw[0] - M) : 0.f;
+      den = fmaf(e, sw[1], den);
+      num = fmaf(e, sw[2 + d], num);
+    }
+    float* dst = ws + (((size_t)b * Hq + kvh * G + hh) * nsplit + split) * (D + 2);
+    dst[2 + d] = num;
+    if (d == 0) {
+      dst[0] = M;
+      dst[1] = den;
+    }
+  }
+}
+
+// Merge of the bf16 pass: like decode_merge_kernel but the partial maxima are
+// in the log2 domain (scores pre-multiplied by scale * log2(e)).
+template <int D>
+__global__ __launch_bounds__(D) void decode_merge2_kernel(const float* __restrict__ ws,
+                                                          const int32_t* __restrict__ kv_lens, bf16* __restrict__ out,
+                                                          int Hq, int max_kv, int nsplit) {
+  const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
+  const int L = min(max(kv_lens[b], 0), max_kv);
+  const int ns = (L + KCH - 1) / KCH;
+  const float* src = ws + ((size_t)b * Hq + h) * nsplit * (D + 2);
+  float M = -INFINITY;
+  for (int c = 0; c < ns; c++) M = fmaxf(M, src[c * (D + 2)]);
+  float num = 0.f, den = 0.f;
+  for (int c = 0; c < ns; c++) {
+    const float e = fast_exp2(src[c * (D + 2)] - M);
+    den = fmaf(e, src[c * (D + 2) + 1], den);
+    num = fmaf(e, src[c * (D + 2) + 2 + d], num);
+  }
+  out[((size_t)b * Hq + h) * D + d] = (bf16)(ns > 0 ? num / den : 0.f);
+}
+
 template <typename T, int D>
 static void launch_decode_t(const void* q, const void* kc, const void* vc, const int32_t* kv_lens, void* out, int B,
                             int Hq, int Hkv, int max_kv, float scale, void* ws, hipStream_t st) {
@@ -123,11 +339,22 @@ static void launch_decode_t(const void* q, const void* kc, const void* vc, const
                      Hq, max_kv, nch);
 }
 
+template <int D>
+static void launch_decode_bf16(const void* q, const void* kc, const void* vc, const int32_t* kv_lens, void* out,
+                               int B, int Hq, int Hkv, int max_kv, float scale, void* ws, hipStream_t st) {
+  const int nsplit = (max_kv + KCH - 1) / KCH;
+  const float c_log2 = (float)((double)scale * 1.4426950408889634);
+  hipLaunchKernelGGL(decode_mfma_kernel<D>, dim3(nsplit, Hkv, B), dim3(64 * DW), 0, st, (const bf16*)q,
+                     (const bf16*)kc, (const bf16*)vc, kv_lens, (float*)ws, Hq, Hkv, max_kv, nsplit, c_log2);
+  hipLaunchKernelGGL(decode_merge2_kernel<D>, dim3(Hq, B), dim3(D), 0, st, (const float*)ws, kv_lens, (bf16*)out, Hq,
+                     max_kv, nsplit);
+}
+
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* kv_lens, void* out, int B,
                          int Hq, int Hkv, int D, int max_kv, float scale, bool bf16_io, void* ws, hipStream_t st) {
   if (bf16_io) {
-    if (D == 64) launch_decode_t<bf16, 64>(q, kc, vc, kv_lens, out, B, Hq, Hkv, max_kv, scale, ws, st);
-    else launch_decode_t<bf16, 128>(q, kc, vc, kv_lens, out, B, Hq, Hkv, max_kv, scale, ws, st);
+    if (D == 64) launch_decode_bf16<64>(q, kc, vc, kv_lens, out, B, Hq, Hkv, max_kv, scale, ws, st);
+    else launch_decode_bf16<128>(q, kc, vc, kv_lens, out, B, Hq, Hkv, max_kv, scale, ws, st);
   } else {
     if (D == 64) launch_decode_t<float, 64>(q, kc, vc, kv_lens, out, B, Hq, Hkv, max_kv, scale, ws, st);
     else launch_decode_t<float, 128>(q, kc, vc, kv_lens, out, B, Hq, Hkv, max_kv, scale, ws, st);

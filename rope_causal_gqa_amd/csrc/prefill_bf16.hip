@@ -6,15 +6,20 @@
 // weights @ V; query head h reads K/V head h / G (repeat_kv).
 //
 // Design (one workgroup = 4 waves = 128 query rows of one (batch, head)):
-//  * K/V tiles of 64 keys are staged in LDS with an XOR swizzle of 16-byte
-//    chunks (chunk ^ row) so both read patterns below are bank-conflict free.
+//  * K/V tiles of 64 keys are double-buffered in LDS and filled with direct
+//    global->LDS loads (global_load_lds_dwordx4) one tile ahead of the math,
+//    with an XOR swizzle of 16-byte chunks (chunk ^ row) so both read
+//    patterns below are bank-conflict free.  One barrier per tile.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K rows are the A operand (read straight from LDS), the wave's 32 query
 //    rows are the B operand (held in registers for the whole kernel).  In the
 //    output layout every lane then owns ONE query row (lane % 32) and 32 of
 //    the tile's 64 keys; the other 32 sit in lane ^ 32, so row max / row sum
 //    need one v_permlane32_swap and no LDS.
-//  * Online softmax in the exp2 domain with fp32 running max / sum per lane.
+//  * Online softmax in the exp2 domain with fp32 running max / sum per lane;
+//    the scale is folded into one FMA before the exp, and the reference max
+//    only moves when a row's max grows by more than 2^8 (lazy rescale), so
+//    the O rescale is skipped on almost every tile.
 //  * O^T = V^T P^T, again 32x32x16: P^T comes straight from the score
 //    registers (converted to bf16; the MFMA's k index is permuted to match the
 //    score layout), V^T is read from the row-major V tile with the gfx950 LDS
@@ -32,21 +37,29 @@ namespace {
 constexpr int BM = 128;  // query rows per workgroup (32 per wave)
 constexpr int BN = 64;   // keys per K/V tile
 constexpr int NT = 256;  // threads per workgroup
+constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (log2 units)
 }  // namespace
 
+__device__ __forceinline__ void lds_dma16(const void* g, bf16* l) {
+  __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3)))*)(l), 16, 0, 0);
+}
+
 template <int D>
-__global__ __launch_bounds__(NT) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
-                                                          const bf16* __restrict__ v, bf16* __restrict__ out,
-                                                          int S, int Hq, int Hkv, int causal, float c_log2) {
+__global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+                                                             const bf16* __restrict__ v, bf16* __restrict__ out,
+                                                             int S, int Hq, int Hkv, int causal, float c_log2) {
   constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the output head dim
   constexpr int CH = D / 8;   // 16-byte chunks per row
   constexpr int SW = CH - 1;  // swizzle mask
   static_assert(CH <= 16 && (CH & (CH - 1)) == 0, "D must be 64 or 128");
-  __shared__ __attribute__((aligned(16))) bf16 sk[BN * D];
-  __shared__ __attribute__((aligned(16))) bf16 sv[BN * D];
+  constexpr int TILE = BN * D;              // elements of one K (or V) tile
+  constexpr int ROWS_PER_LD = 64 / CH;      // rows one wave-wide 16-byte load fills
+  constexpr int LD_PER_WAVE = BN / 4 / ROWS_PER_LD;
+  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * TILE];  // [buffer][K | V][BN][D]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int wu = __builtin_amdgcn_readfirstlane(w);
   const int col = lane & 31, hf = lane >> 5;
   const int bh = blockIdx.x, b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / (Hq / Hkv);
@@ -66,6 +79,25 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(const bf16* __restrict
     for (int ks = 0; ks < KS; ks++) qf[ks] = bf16x8{};
   }
 
+  // Tile loader: wave w fills tile rows [16 w, 16 w + 16) of K and V with
+  // direct global->LDS loads.  Lane p of a load lands at physical chunk
+  // p % CH of row p / CH, so it fetches the logical chunk that the swizzle
+  // puts there.  Keys past S are clamped to S-1 (finite data; masked later).
+  const int lrow = lane / CH, lpc = lane % CH;
+  auto issue = [&](int t, int buf) {
+    bf16* kd = lds + buf * 2 * TILE;
+    bf16* vd = kd + TILE;
+#pragma unroll
+    for (int i = 0; i < LD_PER_WAVE; i++) {
+      const int r0 = wu * (BN / 4) + i * ROWS_PER_LD;  // wave-uniform
+      const int r = r0 + lrow;
+      const int key = min(t * BN + r, S - 1);
+      const size_t goff = (size_t)key * kvrs + (size_t)((lpc ^ (r & SW)) << 3);
+      lds_dma16(kb + goff, kd + r0 * D);
+      lds_dma16(vb + goff, vd + r0 * D);
+    }
+  };
+
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; db++) o[db] = f32x16{};
@@ -80,86 +112,87 @@ __global__ __launch_bounds__(NT) void prefill_bf16_kernel(const bf16* __restrict
   const int vrow_base = 4 * hf + (r16 >> 2);
   const int vcol_base = 16 * (g & 1) + 4 * (r16 & 3);
 
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
   for (int t = 0; t < ntiles; t++) {
     const int kv0 = t * BN;
-    __syncthreads();  // previous tile fully consumed
-    for (int idx = tid; idx < BN * CH; idx += NT) {
-      const int r = idx / CH, c = idx - r * CH, key = kv0 + r;
-      bf16x8 kk{}, vv{};
-      if (key < S) {
-        kk = reinterpret_cast<const bf16x8*>(kb + (size_t)key * kvrs)[c];
-        vv = reinterpret_cast<const bf16x8*>(vb + (size_t)key * kvrs)[c];
-      }
-      const int off = r * D + ((c ^ (r & SW)) << 3);
-      *reinterpret_cast<bf16x8*>(sk + off) = kk;
-      *reinterpret_cast<bf16x8*>(sv + off) = vv;
-    }
-    __syncthreads();
-    if (causal && kv0 > wrow_hi) continue;  // whole tile masked for this wave
+    const int buf = t & 1;
+    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
+    if (!(causal && kv0 > wrow_hi)) {  // else the whole tile is masked for this wave
+      const bf16* sk = lds + buf * 2 * TILE;
+      const bf16* sv = sk + TILE;
 
-    // S^T = K Q^T: two 32-key blocks
-    f32x16 s[2];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; kb2++) {
-      s[kb2] = f32x16{};
-      const int r = kb2 * 32 + col;
+      // S^T = K Q^T: two 32-key blocks, chains interleaved
+      f32x16 s[2] = {f32x16{}, f32x16{}};
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) {
-        const int c = 2 * ks + hf;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (r & SW)) << 3));
-        s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
-      }
-    }
-
-    // scale into the log2 domain, mask, row max
-    const bool need_mask = (causal && kv0 + BN - 1 > wrow_lo) || (kv0 + BN > S);
-    float mx = -INFINITY;
 #pragma unroll
-    for (int kb2 = 0; kb2 < 2; kb2++) {
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        float x = s[kb2][i] * c_log2;
-        if (need_mask) {
-          const int key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-          if (key >= S || (causal && key > qrow)) x = -INFINITY;
+        for (int kb2 = 0; kb2 < 2; kb2++) {
+          const int r = kb2 * 32 + col;
+          const int c = 2 * ks + hf;
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (r & SW)) << 3));
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
         }
-        s[kb2][i] = x;
-        mx = fmaxf(mx, x);
       }
-    }
-    mx = half_swap_max(mx);
-    const float m_new = fmaxf(m_run, mx);
-    const float m_base = (m_new == -INFINITY) ? 0.f : m_new;
-    const float alpha = fast_exp2(m_run - m_base);
-    float psum = 0.f;
-    bf16x8 pf[4];
-#pragma unroll
-    for (int kb2 = 0; kb2 < 2; kb2++) {
-#pragma unroll
-      for (int i = 0; i < 16; i++) {
-        const float p = fast_exp2(s[kb2][i] - m_base);
-        psum += p;
-        pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)p;
-      }
-    }
-    l_run = l_run * alpha + psum;
-    m_run = m_new;
-#pragma unroll
-    for (int db = 0; db < DB; db++) o[db] *= alpha;
 
-    // O^T += V^T P^T over four 16-key chunks
+      // mask (diagonal / tail tiles only) and row max on raw scores
+      if ((causal && kv0 + BN - 1 > wrow_lo) || kv0 + BN > S) {
 #pragma unroll
-    for (int kc = 0; kc < 4; kc++) {
-      const int row1 = 16 * kc + vrow_base, row2 = row1 + 8;
+        for (int kb2 = 0; kb2 < 2; kb2++)
 #pragma unroll
-      for (int db = 0; db < DB; db++) {
-        const int cc = 32 * db + vcol_base;
-        const bf16* p1 = sv + row1 * D + ((((cc >> 3) ^ (row1 & SW))) << 3) + (cc & 7);
-        const bf16* p2 = sv + row2 * D + ((((cc >> 3) ^ (row2 & SW))) << 3) + (cc & 7);
-        const bf16x8 a = cat8(lds_read_tr16(p1), lds_read_tr16(p2));
-        o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
+          for (int i = 0; i < 16; i++) {
+            const int key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+            if (key >= S || (causal && key > qrow)) s[kb2][i] = -INFINITY;
+          }
+      }
+      float mx = s[0][0];
+#pragma unroll
+      for (int i = 1; i < 16; i++) mx = fmaxf(mx, s[0][i]);
+#pragma unroll
+      for (int i = 0; i < 16; i++) mx = fmaxf(mx, s[1][i]);
+      mx = half_swap_max(mx);
+
+      // lazy rescale: move the reference max only when some row grew by more
+      // than 2^kRescaleLog2 (exact either way: O and l share the reference)
+      const float m_new = fmaxf(m_run, mx);
+      if (__any((m_new - m_run) * c_log2 > kRescaleLog2)) {
+        const float alpha = fast_exp2((m_run - m_new) * c_log2);
+        l_run *= alpha;
+#pragma unroll
+        for (int db = 0; db < DB; db++) o[db] *= alpha;
+        m_run = m_new;
+      }
+      const float mc = m_run * c_log2;
+      float psum = 0.f;
+      bf16x8 pf[4];
+#pragma unroll
+      for (int kb2 = 0; kb2 < 2; kb2++) {
+#pragma unroll
+        for (int i = 0; i < 16; i++) {
+          const float p = fast_exp2(fmaf(s[kb2][i], c_log2, -mc));
+          psum += p;
+          pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)p;
+        }
+      }
+      l_run += psum;
+
+      // O^T += V^T P^T over four 16-key chunks
+#pragma unroll
+      for (int kc = 0; kc < 4; kc++) {
+        const int row1 = 16 * kc + vrow_base, row2 = row1 + 8;
+#pragma unroll
+        for (int db = 0; db < DB; db++) {
+          const int cc = 32 * db + vcol_base;
+          const bf16* p1 = sv + row1 * D + (((cc >> 3) ^ (row1 & SW)) << 3) + (cc & 7);
+          const bf16* p2 = sv + row2 * D + (((cc >> 3) ^ (row2 & SW)) << 3) + (cc & 7);
+          const bf16x8 a = cat8(lds_read_tr16(p1), lds_read_tr16(p2));
+          o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
+        }
       }
     }
+    __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
+    __syncthreads();                // ... and everyone's; tile t fully consumed
   }
 
   const float l_tot = half_swap_sum(l_run);

@@ -29,6 +29,20 @@ __device__ __forceinline__ float half_swap_sum(float x) {
   return __uint_as_float(r[0]) + __uint_as_float(r[1]);
 }
 
+// XOR mask applied to the 16-byte chunk index of LDS row r (K/V tiles with
+// 256-byte rows).  LDS has 64 four-byte banks and serves 256 bytes per cycle;
+// the mask makes each access pattern of the kernels cover all banks:
+//  * 16 consecutive rows at one logical chunk (K operand reads): the mask is a
+//    bijection on r % 16, so the 16 chunks land on distinct bank groups;
+//  * a transpose read half-wave touching 4 aligned rows x 64 bytes (32x32
+//    layouts): bits 2-3 of the mask differ across the 4 rows;
+//  * a transpose read half-wave touching 8 aligned rows x 32 bytes (16x16
+//    layouts): bits 1-3 of the mask differ across the 8 rows.
+__device__ __forceinline__ int row_swizzle(int r) {
+  const int r0 = r & 1, r1 = (r >> 1) & 1, r2 = (r >> 2) & 1, r3 = (r >> 3) & 1;
+  return r3 | (r2 << 1) | ((r0 ^ r2) << 2) | ((r1 ^ r3) << 3);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // LDS transpose read: lane i of each 16-lane group receives, as 4 consecutive

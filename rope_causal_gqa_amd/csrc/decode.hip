@@ -196,7 +196,7 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
 #pragma unroll
     for (int p = 0; p < LD_PER_LANE; p++) {
       const int idx = p * 64 + lane, r = idx / CH, c = idx - r * CH;
-      const int off = r * D + ((c ^ (r & SW)) << 3);
+      const int off = r * D + ((c ^ (row_swizzle(r) & SW)) << 3);
       *reinterpret_cast<bf16x8*>(sk + off) = pk[p];
       *reinterpret_cast<bf16x8*>(sv + off) = pv[p];
     }
@@ -224,7 +224,7 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
 #pragma unroll
       for (int ks = 0; ks < KSTEP; ks++) {
         const int c = 4 * ks + g;
-        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (r & SW)) << 3));
+        const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (row_swizzle(r) & SW)) << 3));
         s[kb2] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, qf[ks], s[kb2], 0, 0, 0);
       }
     }
@@ -261,8 +261,8 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
     for (int db = 0; db < DBLK; db++) {
       o[db] *= alpha;
       const int cc = 16 * db + vcb;
-      const bf16* p1 = sv + vr1 * D + (((cc >> 3) ^ (vr1 & SW)) << 3) + (cc & 7);
-      const bf16* p2 = sv + vr2 * D + (((cc >> 3) ^ (vr2 & SW)) << 3) + (cc & 7);
+      const bf16* p1 = sv + vr1 * D + (((cc >> 3) ^ (row_swizzle(vr1) & SW)) << 3) + (cc & 7);
+      const bf16* p2 = sv + vr2 * D + (((cc >> 3) ^ (row_swizzle(vr2) & SW)) << 3) + (cc & 7);
       const bf16x8 a = cat8(lds_read_tr16(p1), lds_read_tr16(p2));
       o[db] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, pf, o[db], 0, 0, 0);
     }

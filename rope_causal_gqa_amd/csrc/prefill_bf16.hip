@@ -8,7 +8,7 @@
 // Design (one workgroup = 4 waves = 128 query rows of one (batch, head)):
 //  * K/V tiles of 64 keys are double-buffered in LDS and filled with direct
 //    global->LDS loads (global_load_lds_dwordx4) one tile ahead of the math,
-//    with an XOR swizzle of 16-byte chunks (chunk ^ row) so both read
+//    with a row-dependent XOR swizzle of 16-byte chunks so all three read
 //    patterns below are bank-conflict free.  One barrier per tile.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K rows are the A operand (read straight from LDS), the wave's 32 query
@@ -92,7 +92,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
       const int r0 = wu * (BN / 4) + i * ROWS_PER_LD;  // wave-uniform
       const int r = r0 + lrow;
       const int key = min(t * BN + r, S - 1);
-      const size_t goff = (size_t)key * kvrs + (size_t)((lpc ^ (r & SW)) << 3);
+      const size_t goff = (size_t)key * kvrs + (size_t)((lpc ^ (row_swizzle(r) & SW)) << 3);
       lds_dma16(kb + goff, kd + r0 * D);
       lds_dma16(vb + goff, vd + r0 * D);
     }
@@ -131,7 +131,7 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
         for (int kb2 = 0; kb2 < 2; kb2++) {
           const int r = kb2 * 32 + col;
           const int c = 2 * ks + hf;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (r & SW)) << 3));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (row_swizzle(r) & SW)) << 3));
           s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
         }
       }
@@ -184,8 +184,8 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
 #pragma unroll
         for (int db = 0; db < DB; db++) {
           const int cc = 32 * db + vcol_base;
-          const bf16* p1 = sv + row1 * D + (((cc >> 3) ^ (row1 & SW)) << 3) + (cc & 7);
-          const bf16* p2 = sv + row2 * D + (((cc >> 3) ^ (row2 & SW)) << 3) + (cc & 7);
+          const bf16* p1 = sv + row1 * D + (((cc >> 3) ^ (row_swizzle(row1) & SW)) << 3) + (cc & 7);
+          const bf16* p2 = sv + row2 * D + (((cc >> 3) ^ (row_swizzle(row2) & SW)) << 3) + (cc & 7);
           const bf16x8 a = cat8(lds_read_tr16(p1), lds_read_tr16(p2));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
         }

@@ -103,6 +103,21 @@ def main():
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
 
+    # Reference point for HBM: a plain 1 GiB device-to-device copy (also the
+    # calibration kernel for the FETCH_SIZE / WRITE_SIZE counters).
+    ca = torch.ones(1 << 28, dtype=torch.float32, device=dev)
+    cb = torch.empty_like(ca)
+    cb.copy_(ca)
+    torch.cuda.synchronize()
+    c0, c1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    c0.record()
+    for _ in range(3):
+        cb.copy_(ca)
+    c1.record()
+    torch.cuda.synchronize()
+    copy_gbps = 3 * 2 * ca.numel() * 4 / (c0.elapsed_time(c1) * 1e-3) / 1e9
+    del ca, cb
+
     # ---- prefill inputs (LLaMA-7B-shaped)
     wp = W.WORKLOADS["c3"]
     tb = lambda a: torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
@@ -199,6 +214,7 @@ def main():
                                 "traffic": _traffic("decode_c5", DECODE_KERNEL_SRC)}},
         "rope": {"value": round(rope_bytes / (rope_ms.mean() * 1e-3) / 1e9, 1), "unit": "GB/s",
                  "launch_ms": round(float(rope_ms.mean()), 4)},
+        "hbm_copy_gbps": round(copy_gbps, 1),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -113,21 +113,36 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
   out[((size_t)b * Hq + h) * D + d] = (T)(n > 0 ? num / den : 0.f);
 }
 
-// Pass 1, bf16 form, on matrix cores.  One workgroup = 4 waves handles one
+// Pass 1, bf16 form, on matrix cores.  One workgroup = DW waves handles one
 // split of KCH keys of one (batch, KV head) for all G <= 16 query heads of the
 // group, so each K/V row is read from HBM once per group.  Each wave streams
-// its own 32-key tiles (tiles w, w+4, ... of the split) through a private LDS
+// its own 32-key tiles (tiles w, w+DW, ... of the split) through a private LDS
 // region, with the next tile prefetched into registers while the current one
-// is computed; waves never wait for each other until the final combine.
+// is computed; waves never wait for each other until the final combine.  The
+// cache is read with non-temporal loads: it is streamed once per call, so
+// keeping it out of L2 / Infinity Cache leaves them to the partial states.
+// Defaults (2048-key splits, 8 waves, non-temporal) were picked by a sweep on
+// the B=64 Hq=64 Hkv=8 D=128 workload with lengths in [512, 8192]:
+// 512/4/temporal 242 us, 1024/8/temporal 235 us, 2048/8/non-temporal 208 us.
 //   S^T (32 keys x 16 heads) = K Q^T   v_mfma_f32_16x16x32_bf16, K from LDS
 //   O^T (D x 16 heads)      += V^T P^T  same MFMA, V^T via the LDS transpose read
 // In both outputs a lane owns one head (lane % 16), so the online-softmax
 // rescale is one multiply per accumulator.  The 4 waves' states are combined
 // in LDS and written as one partial state per (split, head).
+#ifndef RCGQA_DECODE_SPLIT
+#define RCGQA_DECODE_SPLIT 2048
+#endif
+#ifndef RCGQA_DECODE_NT
+#define RCGQA_DECODE_NT 1
+#endif
+#ifndef RCGQA_DECODE_WAVES
+#define RCGQA_DECODE_WAVES 8
+#endif
 namespace {
-constexpr int KCH = 512;   // keys per split
-constexpr int TK = 32;     // keys per wave tile
-constexpr int DW = 4;      // waves per workgroup
+constexpr int KCH = RCGQA_DECODE_SPLIT;  // keys per split (>= KC, so the workspace bound holds)
+constexpr int TK = 32;                   // keys per wave tile
+constexpr int DW = RCGQA_DECODE_WAVES;   // waves per workgroup
+static_assert(KCH >= KC && KCH % TK == 0, "split must be a multiple of the tile and at least KC");
 }
 
 template <int D>
@@ -184,8 +199,13 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
       const int idx = p * 64 + lane, r = idx / CH, c = idx - r * CH;
       const int key = t0 + r;
       if (key < kend) {
+#if RCGQA_DECODE_NT
+        pk[p] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kb + (size_t)key * D) + c);
+        pv[p] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vb + (size_t)key * D) + c);
+#else
         pk[p] = reinterpret_cast<const bf16x8*>(kb + (size_t)key * D)[c];
         pv[p] = reinterpret_cast<const bf16x8*>(vb + (size_t)key * D)[c];
+#endif
       } else {
         pk[p] = bf16x8{};
         pv[p] = bf16x8{};
@@ -308,23 +328,44 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
   }
 }
 
-// Merge of the bf16 pass: like decode_merge_kernel but the partial maxima are
-// in the log2 domain (scores pre-multiplied by scale * log2(e)).
+// Merge of the bf16 pass: the partial maxima are in the log2 domain (scores
+// pre-multiplied by scale * log2(e)).  Splits are taken in batches of MB whose
+// loads are all issued before the batch is folded in (online, fixed order),
+// so the pass is bound by bandwidth rather than by one load latency per split.
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge2_kernel(const float* __restrict__ ws,
                                                           const int32_t* __restrict__ kv_lens, bf16* __restrict__ out,
                                                           int Hq, int max_kv, int nsplit) {
+  constexpr int MB = 8;
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int L = min(max(kv_lens[b], 0), max_kv);
   const int ns = (L + KCH - 1) / KCH;
   const float* src = ws + ((size_t)b * Hq + h) * nsplit * (D + 2);
-  float M = -INFINITY;
-  for (int c = 0; c < ns; c++) M = fmaxf(M, src[c * (D + 2)]);
-  float num = 0.f, den = 0.f;
-  for (int c = 0; c < ns; c++) {
-    const float e = fast_exp2(src[c * (D + 2)] - M);
-    den = fmaf(e, src[c * (D + 2) + 1], den);
-    num = fmaf(e, src[c * (D + 2) + 2 + d], num);
+  float M = -INFINITY, den = 0.f, num = 0.f;
+  for (int c0 = 0; c0 < ns; c0 += MB) {
+    float m[MB], l[MB], a[MB];
+#pragma unroll
+    for (int i = 0; i < MB; i++) {
+      const bool ok = c0 + i < ns;
+      const float* p = src + (size_t)(ok ? c0 + i : 0) * (D + 2);
+      m[i] = ok ? p[0] : -INFINITY;
+      l[i] = ok ? p[1] : 0.f;
+      a[i] = ok ? p[2 + d] : 0.f;
+    }
+    float mb = m[0];
+#pragma unroll
+    for (int i = 1; i < MB; i++) mb = fmaxf(mb, m[i]);
+    const float mn = fmaxf(M, mb);            // finite: split c0 holds a valid key
+    const float sc = fast_exp2(M - mn);       // 0 on the first batch
+    den *= sc;
+    num *= sc;
+#pragma unroll
+    for (int i = 0; i < MB; i++) {
+      const float e = fast_exp2(m[i] - mn);   // 0 for the padding entries
+      den = fmaf(e, l[i], den);
+      num = fmaf(e, a[i], num);
+    }
+    M = mn;
   }
   out[((size_t)b * Hq + h) * D + d] = (bf16)(ns > 0 ? num / den : 0.f);
 }

@@ -63,6 +63,8 @@ DEC_EDGE = [
     (2, 8, 8, 64, 700, [700, 2], "bf16"),
     (2, 16, 1, 128, 300, [0, 1000], "bf16"),          # empty row and clamped length
     (5, 32, 2, 128, 2049, [2049, 7, 1536, 100, 1], "bf16"),
+    (2, 8, 1, 128, 20000, [20000, 6145], "bf16"),     # > 8 splits: merge batches
+    (2, 16, 1, 128, 4096, [4096, 2048], "bf16"),      # exact split multiples
     (2, 8, 2, 64, 400, [399, 1], "fp32"),
     (3, 4, 4, 128, 513, [513, 256, 0], "fp32"),
 ]

@@ -43,6 +43,13 @@ __device__ __forceinline__ int row_swizzle(int r) {
   return r3 | (r2 << 1) | ((r0 ^ r2) << 2) | ((r1 ^ r3) << 3);
 }
 
+// acc + a + b for two bf16 values, in one v_dot2c_f32_bf16 (products by 1.0 are exact).
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float bf16_pair_sum(bf16 a, bf16 b, float acc) {
+  const bf16x2 one = {(bf16)1.0f, (bf16)1.0f};
+  return __builtin_amdgcn_fdot2_f32_bf16(bf16x2{a, b}, one, acc, false);
+}
+
 __device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
 
 // LDS transpose read: lane i of each 16-lane group receives, as 4 consecutive

@@ -192,7 +192,7 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
 
   // register prefetch of one tile: lane loads chunk (lane % CH) of rows lane / CH + (64 / CH) * p
   bf16x8 pk[LD_PER_LANE], pv[LD_PER_LANE];
-  auto load_tile = [&](int t) {
+  auto load_tile = [&](int t)  __attribute__((always_inline)) {
     const int t0 = k0 + t * TK;
 #pragma unroll
     for (int p = 0; p < LD_PER_LANE; p++) {
@@ -212,7 +212,7 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
       }
     }
   };
-  auto store_tile = [&]() {
+  auto store_tile = [&]()  __attribute__((always_inline)) {
 #pragma unroll
     for (int p = 0; p < LD_PER_LANE; p++) {
       const int idx = p * 64 + lane, r = idx / CH, c = idx - r * CH;

@@ -5,7 +5,8 @@
 // softmax kept in fp32 (also "Llama2 Transformer架构解析与优化实践" section 3.2),
 // weights @ V; query head h reads K/V head h / G (repeat_kv).
 //
-// Design (one workgroup = 4 waves = 128 query rows of one (batch, head)):
+// Design (one workgroup = NW waves = 32 NW query rows of one (batch, head);
+// NW = 8 when the grid is large enough, else 4):
 //  * K/V tiles of 64 keys are double-buffered in LDS and filled with direct
 //    global->LDS loads (global_load_lds_dwordx4) one tile ahead of the math,
 //    with a row-dependent XOR swizzle of 16-byte chunks so all three read
@@ -28,26 +29,31 @@
 //  * Causal: tiles past the block's last row are never loaded; a wave skips
 //    the math of tiles past its own last row; only diagonal / tail tiles pay
 //    for per-element masking.  Heaviest query tiles are dispatched first.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
 namespace rcgqa {
 
 namespace {
-constexpr int BM = 128;  // query rows per workgroup (32 per wave)
-constexpr int BN = 64;   // keys per K/V tile
-constexpr int NT = 256;  // threads per workgroup
-constexpr float kRescaleLog2 = 8.f;  // lazy rescale threshold (log2 units)
+constexpr int BN = 64;                   // keys per K/V tile
+constexpr float kRescaleLog2 = 8.f;      // lazy rescale threshold (log2 units)
+constexpr int PREF = 4;                  // K-operand LDS reads kept ahead of the MFMAs
+// instruction classes of __builtin_amdgcn_sched_group_barrier
+constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 }  // namespace
 
 __device__ __forceinline__ void lds_dma16(const void* g, bf16* l) {
   __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3)))*)(l), 16, 0, 0);
 }
 
-template <int D>
-__global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
+template <int D, int NW>
+__global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
-                                                             int S, int Hq, int Hkv, int causal, float c_log2) {
+                                                             int S, int Hq, int Hkv, int causal, float c_log2,
+                                                             int nqt, int npairs) {
+  constexpr int BM = 32 * NW; // query rows per workgroup (32 per wave)
   constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the output head dim
   constexpr int CH = D / 8;   // 16-byte chunks per row
@@ -55,18 +61,33 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
   static_assert(CH <= 16 && (CH & (CH - 1)) == 0, "D must be 64 or 128");
   constexpr int TILE = BN * D;              // elements of one K (or V) tile
   constexpr int ROWS_PER_LD = 64 / CH;      // rows one wave-wide 16-byte load fills
-  constexpr int LD_PER_WAVE = BN / 4 / ROWS_PER_LD;
+  constexpr int LD_PER_WAVE = BN / NW / ROWS_PER_LD;
+  static_assert(LD_PER_WAVE >= 1, "tile rows per wave");
   __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * TILE];  // [buffer][K | V][BN][D]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
   const int col = lane & 31, hf = lane >> 5;
-  const int bh = blockIdx.x, b = bh / Hq, h = bh - b * Hq;
+  // Work item of this workgroup.  The work list is ordered (batch, query head,
+  // query-tile slot), so consecutive items share a head and consecutive heads
+  // share a KV head.  The hardware hands consecutive workgroup ids to the 8
+  // XCDs in turn; each XCD is given one contiguous eighth of the list, so the
+  // query tiles (and GQA heads) that reuse a K/V stream run on one XCD and
+  // hit its L2.  A slot is either one query tile or, when there are enough
+  // workgroups to fill the GPU (npairs < nqt), the pair (nqt-1-p, p): a
+  // heavy and a light causal tile, so every workgroup does the same work.
+  const int total = (int)gridDim.x;
+  const int wid = (int)blockIdx.x;
+  const int item = (total & 7) == 0 ? (wid & 7) * (total >> 3) + (wid >> 3) : wid;
+  const int bh = item / npairs, slot = item - bh * npairs;
+  const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / (Hq / Hkv);
-  const int q0 = ((int)gridDim.y - 1 - (int)blockIdx.y) * BM;  // heaviest tiles first
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
   const bf16* kb = k + (size_t)b * S * kvrs + (size_t)kvh * D;
   const bf16* vb = v + (size_t)b * S * kvrs + (size_t)kvh * D;
+  const int qt_first = npairs < nqt ? nqt - 1 - slot : slot;
+  const int npass = (npairs < nqt && slot != nqt - 1 - slot) ? 2 : 1;
+  auto run_qtile = [&](const int q0) __attribute__((always_inline)) {
 
   const int qrow = q0 + w * 32 + col;  // this lane's query row
   bf16x8 qf[KS];
@@ -79,22 +100,42 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
     for (int ks = 0; ks < KS; ks++) qf[ks] = bf16x8{};
   }
 
-  // Tile loader: wave w fills tile rows [16 w, 16 w + 16) of K and V with
+  // Tile loader: wave w fills tile rows [w BN/NW, (w+1) BN/NW) of K and V with
   // direct global->LDS loads.  Lane p of a load lands at physical chunk
   // p % CH of row p / CH, so it fetches the logical chunk that the swizzle
   // puts there.  Keys past S are clamped to S-1 (finite data; masked later).
   const int lrow = lane / CH, lpc = lane % CH;
-  auto issue = [&](int t, int buf) {
+  // Byte offsets of this lane's loads inside a tile do not depend on the tile:
+  // computed once (32-bit), so a full tile costs one scalar base update and no
+  // per-lane address arithmetic.  Only a tile crossing S clamps per lane.
+  uint32_t loff[LD_PER_WAVE];
+#pragma unroll
+  for (int i = 0; i < LD_PER_WAVE; i++) {
+    const int r = wu * (BN / NW) + i * ROWS_PER_LD + lrow;
+    loff[i] = (uint32_t)(r * (int)kvrs + ((lpc ^ (row_swizzle(r) & SW)) << 3)) * (uint32_t)sizeof(bf16);
+  }
+  auto issue = [&](int t, int buf)  __attribute__((always_inline)) {
     bf16* kd = lds + buf * 2 * TILE;
     bf16* vd = kd + TILE;
+    if (t * BN + BN <= S) {
+      const char* kt = reinterpret_cast<const char*>(kb + (size_t)t * BN * kvrs);
+      const char* vt = reinterpret_cast<const char*>(vb + (size_t)t * BN * kvrs);
 #pragma unroll
-    for (int i = 0; i < LD_PER_WAVE; i++) {
-      const int r0 = wu * (BN / 4) + i * ROWS_PER_LD;  // wave-uniform
-      const int r = r0 + lrow;
-      const int key = min(t * BN + r, S - 1);
-      const size_t goff = (size_t)key * kvrs + (size_t)((lpc ^ (row_swizzle(r) & SW)) << 3);
-      lds_dma16(kb + goff, kd + r0 * D);
-      lds_dma16(vb + goff, vd + r0 * D);
+      for (int i = 0; i < LD_PER_WAVE; i++) {
+        const int r0 = wu * (BN / NW) + i * ROWS_PER_LD;  // wave-uniform
+        lds_dma16(kt + loff[i], kd + r0 * D);
+        lds_dma16(vt + loff[i], vd + r0 * D);
+      }
+    } else {
+#pragma unroll
+      for (int i = 0; i < LD_PER_WAVE; i++) {
+        const int r0 = wu * (BN / NW) + i * ROWS_PER_LD;
+        const int r = r0 + lrow;
+        const int key = min(t * BN + r, S - 1);
+        const size_t goff = (size_t)key * kvrs + (size_t)((lpc ^ (row_swizzle(r) & SW)) << 3);
+        lds_dma16(kb + goff, kd + r0 * D);
+        lds_dma16(vb + goff, vd + r0 * D);
+      }
     }
   };
 
@@ -111,13 +152,27 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
   const int r16 = lane & 15, g = lane >> 4;
   const int vrow_base = 4 * hf + (r16 >> 2);
   const int vcol_base = 16 * (g & 1) + 4 * (r16 & 3);
+  // Per-lane byte offsets of the operand reads inside a tile.  The row block
+  // (kb2, kc) and the buffer only add immediates: the swizzle depends on
+  // row % 16, which those blocks do not change.
+  int koff[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++)
+    koff[ks] = (col * D + (((2 * ks + hf) ^ (row_swizzle(col) & SW)) << 3)) * (int)sizeof(bf16);
+  int voff[DB][2];
+#pragma unroll
+  for (int db = 0; db < DB; db++)
+#pragma unroll
+    for (int j = 0; j < 2; j++) {
+      const int row = vrow_base + 8 * j, cc = 32 * db + vcol_base;
+      voff[db][j] = (row * D + (((cc >> 3) ^ (row_swizzle(row) & SW)) << 3) + (cc & 7)) * (int)sizeof(bf16);
+    }
 
-  issue(0, 0);
-  __builtin_amdgcn_s_waitcnt(0);
-  __syncthreads();
-  for (int t = 0; t < ntiles; t++) {
+  // One tile; `bufc` carries the buffer parity at compile time so every LDS
+  // address below is a per-lane constant plus an immediate offset.
+  auto tile_step = [&](int t, auto bufc)  __attribute__((always_inline)) {
+    constexpr int buf = decltype(bufc)::value;
     const int kv0 = t * BN;
-    const int buf = t & 1;
     if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
     if (!(causal && kv0 > wrow_hi)) {  // else the whole tile is masked for this wave
       const bf16* sk = lds + buf * 2 * TILE;
@@ -129,11 +184,19 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
       for (int ks = 0; ks < KS; ks++) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; kb2++) {
-          const int r = kb2 * 32 + col;
-          const int c = 2 * ks + hf;
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(sk + r * D + ((c ^ (row_swizzle(r) & SW)) << 3));
+          const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(sk) + koff[ks] +
+                                                            kb2 * 32 * D * (int)sizeof(bf16));
           s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
         }
+      }
+      if (PREF > 0) {
+        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PREF, 0);
+#pragma unroll
+        for (int i = 0; i < 2 * KS - PREF; i++) {
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        }
+        __builtin_amdgcn_sched_group_barrier(kSchedMfma, PREF, 0);
       }
 
       // mask (diagonal / tail tiles only) and row max on raw scores
@@ -164,35 +227,41 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
         m_run = m_new;
       }
       const float mc = m_run * c_log2;
-      float psum = 0.f;
       bf16x8 pf[4];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; kb2++) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) {
-          const float p = fast_exp2(fmaf(s[kb2][i], c_log2, -mc));
-          psum += p;
-          pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)p;
-        }
+        for (int i = 0; i < 16; i++) pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)fast_exp2(fmaf(s[kb2][i], c_log2, -mc));
       }
-      l_run += psum;
+      // row sum of the bf16 weights actually fed to the MFMA (two per dot2)
+      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int j = 0; j < 4; j++)
+#pragma unroll
+        for (int e = 0; e < 4; e++) ps[e] = bf16_pair_sum(pf[j][2 * e], pf[j][2 * e + 1], ps[e]);
+      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
 
       // O^T += V^T P^T over four 16-key chunks
 #pragma unroll
       for (int kc = 0; kc < 4; kc++) {
-        const int row1 = 16 * kc + vrow_base, row2 = row1 + 8;
 #pragma unroll
         for (int db = 0; db < DB; db++) {
-          const int cc = 32 * db + vcol_base;
-          const bf16* p1 = sv + row1 * D + (((cc >> 3) ^ (row_swizzle(row1) & SW)) << 3) + (cc & 7);
-          const bf16* p2 = sv + row2 * D + (((cc >> 3) ^ (row_swizzle(row2) & SW)) << 3) + (cc & 7);
-          const bf16x8 a = cat8(lds_read_tr16(p1), lds_read_tr16(p2));
+          const char* vbase = reinterpret_cast<const char*>(sv) + kc * 16 * D * (int)sizeof(bf16);
+          const bf16x8 a = cat8(lds_read_tr16(reinterpret_cast<const bf16*>(vbase + voff[db][0])),
+                                lds_read_tr16(reinterpret_cast<const bf16*>(vbase + voff[db][1])));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
         }
       }
     }
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
     __syncthreads();                // ... and everyone's; tile t fully consumed
+  };
+  issue(0, 0);
+  __builtin_amdgcn_s_waitcnt(0);
+  __syncthreads();
+  for (int t = 0; t < ntiles; t += 2) {
+    tile_step(t, std::integral_constant<int, 0>{});
+    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>{});
   }
 
   const float l_tot = half_swap_sum(l_run);
@@ -211,18 +280,42 @@ __global__ __launch_bounds__(NT, 2) void prefill_bf16_kernel(const bf16* __restr
       }
     }
   }
+  };  // run_qtile
+  run_qtile(qt_first * BM);
+  if (npass == 2) run_qtile(slot * BM);
+}
+
+template <int NW>
+static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq, int Hkv,
+                      int D, bool causal, float c_log2, int npairs, hipStream_t st) {
+  const int nqt = (S + 32 * NW - 1) / (32 * NW);
+  const dim3 grid((unsigned)((long long)B * Hq * npairs)), block(64 * NW);
+  if (D == 64)
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2, nqt, npairs);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2, nqt, npairs);
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
                                int Hkv, int D, bool causal, float scale, hipStream_t st) {
-  const dim3 grid((unsigned)(B * Hq), (unsigned)((S + BM - 1) / BM)), block(NT);
   const float c_log2 = (float)((double)scale * 1.4426950408889634);
-  if (D == 64)
-    hipLaunchKernelGGL(prefill_bf16_kernel<64>, grid, block, 0, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2);
-  else
-    hipLaunchKernelGGL(prefill_bf16_kernel<128>, grid, block, 0, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2);
+  // Every K/V tile brought into LDS serves the workgroup's query rows, so 8
+  // waves (256 rows) halve the tile traffic per flop against 4 waves (128
+  // rows).  Both run 8 waves per CU (one 8-wave or two 4-wave workgroups).
+  // Causal grids pair heavy and light query tiles so all workgroups do equal
+  // work; 8 waves are used only when that paired grid still has 512
+  // workgroups or more, otherwise 4 waves keep more CUs busy, pairing only
+  // when 512 paired workgroups result.
+  const long long bh = (long long)B * Hq;
+  const int nqt8 = (S + 255) / 256, nqt4 = (S + 127) / 128;
+  if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512) {
+    launch_nw<8>(q, k, v, out, B, S, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, st);
+  } else {
+    const int npairs = (causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512) ? (nqt4 + 1) / 2 : nqt4;
+    launch_nw<4>(q, k, v, out, B, S, Hq, Hkv, D, causal, c_log2, npairs, st);
+  }
   return hipGetLastError();
 }
 

@@ -101,6 +101,39 @@ def test_prefill_edges(B, S, Hq, Hkv, D, causal, dtype):
     check(host64(out), ref, dtype, f"edge B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} c={causal}")
 
 
+# Causal grids with at least 512 paired 256-row tiles take the 8-wave kernel:
+# ragged S, an odd number of 256-row tiles (one unpaired middle tile), D=64.
+BIG = [
+    # B, S, Hq, Hkv, D, heads sampled
+    (8, 1000, 32, 8, 128, [(0, 0), (3, 13), (7, 31)]),
+    (4, 1100, 64, 8, 128, [(0, 1), (2, 40), (3, 63)]),
+    (4, 777, 64, 8, 64, [(0, 0), (1, 22), (3, 57)]),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,heads", BIG)
+def test_prefill_eight_wave_grid(B, S, Hq, Hkv, D, heads):
+    import torch
+    announce(f"prefill 8-wave grid B={B} S={S} Hq={Hq} Hkv={Hkv} D={D}")
+    seed = 5 + B * 7 + S * 13 + Hq * 17 + D
+    q = W.random_case(seed, (B, S, Hq, D), "bf16")
+    k = W.random_case(seed + 1, (B, S, Hkv, D), "bf16")
+    v = W.random_case(seed + 2, (B, S, Hkv, D), "bf16")
+    scale = 1.0 / math.sqrt(D)
+    n = B * S * Hq * D
+    buf = torch.full((n + 2048,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[1024:1024 + n].view(B, S, Hq, D)
+    R.attn_prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, causal=True, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:1024] == 7.0) and torch.all(buf[1024 + n:] == 7.0), "write outside out"
+    got = host64(out)
+    assert np.all(np.isfinite(got))
+    ref = oracle.attention(W.to_f64(q, "bf16"), W.to_f64(k, "bf16"), W.to_f64(v, "bf16"), True, scale,
+                           heads=heads)
+    for b, h in heads:
+        check(got[b, :, h], ref[b, :, h], "bf16", f"8-wave B={B} S={S} b={b} h={h}")
+
+
 def test_prefill_deterministic():
     import torch
     w = W.WORKLOADS["c2b"]

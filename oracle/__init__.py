@@ -10,8 +10,9 @@ blocking, fusion or reordering beyond that definition:
 
 * ``rope``      -- rotary position embedding (frequencies, angles, rotation).
 * ``attention`` -- scaled dot-product attention with a bottom-right causal
-                   mask and grouped-query head sharing, and single-token
-                   decode against a cache.
+                   mask (optionally a sliding window) and grouped-query head
+                   sharing; single-token decode and chunked / variable-length
+                   prefill against a cache.
 
 Pins (tests marked ``not gpu``) tie each function to something other than
 itself: closed forms, invariants, brute-force loops on tiny shapes, a library
@@ -19,7 +20,7 @@ routine the pages name (torch's CPU scaled_dot_product_attention in float64),
 and hand-derived fixtures under ``tests/golden``.
 """
 from .rope import inv_freq, angles, rotate, rope_apply
-from .attention import attention, attention_probs, decode, kv_append
+from .attention import attention, attention_cache, attention_probs, decode, kv_append
 
 __all__ = ["inv_freq", "angles", "rotate", "rope_apply",
-           "attention", "attention_probs", "decode", "kv_append"]
+           "attention", "attention_cache", "attention_probs", "decode", "kv_append"]

@@ -16,7 +16,17 @@ section 1.2 steps 2-4 and section 2 forward steps 4-5):
   "8 query heads share one K/V head" ("Llama2 Transformer架构解析与优化实践",
   section 2.1);
 * decode with a cache ("LLaMA2大语言模型架构详解", section "KV cache"): one new
-  query against all kv_len cached (already rotated) keys and values.
+  query against all kv_len cached (already rotated) keys and values;
+* chunked / variable-length prefill against a cache: a block of Sq new queries
+  of sequence b against its kv_len_b cached rows, the last Sq of which are the
+  block's own keys (the bottom-right alignment above with Sk = kv_len_b; the
+  variable-length support of "【HuggingFace Transformers】LlamaAttention源码解析",
+  section 3.1);
+* sliding window: the flash-attention call of "llama.py — LLaMA 注意力层 Ulysses
+  SP 适配" (section "第二步：RoPE + Flash Attention") passes a ``sliding_window``,
+  never defined on the pages.  Reading: with window W > 0 a query at absolute
+  position p sees only the W most recent positions, keys p - W < j <= p (causal
+  only); W = 0 means no window.
 
 A row whose keys are all masked (possible only when Sq > Sk, or kv_len == 0)
 returns zeros (a reading: the pages never produce such a row).
@@ -36,14 +46,19 @@ def _check(q, k, v):
     return B, Sq, Hq, D, k.shape[1], Hkv
 
 
-def _scores(qh, kh, scale, causal):
-    """scale * qh @ kh^T with the bottom-right causal mask as -inf."""
+def _scores(qh, kh, scale, causal, window=0):
+    """scale * qh @ kh^T with the bottom-right causal mask (and the sliding
+    window, if any) as -inf."""
     Sq, Sk = qh.shape[0], kh.shape[0]
     s = np.float64(scale) * (qh @ kh.T)
     if causal:
-        i = np.arange(Sq)[:, None]
+        pos = np.arange(Sq)[:, None] + (Sk - Sq)   # absolute position of each query
         j = np.arange(Sk)[None, :]
-        s = np.where(j > i + (Sk - Sq), -np.inf, s)
+        s = np.where(j > pos, -np.inf, s)
+        if window > 0:
+            s = np.where(j <= pos - window, -np.inf, s)
+    elif window > 0:
+        raise ValueError("a sliding window needs causal attention")
     return s
 
 
@@ -66,12 +81,13 @@ def attention_probs(q, k, scale, causal, b, h):
     return _softmax_rows(_scores(q[b, :, h, :], k[b, :, h // G, :], scale, causal))
 
 
-def attention(q, k, v, causal, scale, heads=None):
+def attention(q, k, v, causal, scale, heads=None, window=0):
     """out[b, i, h, :] = sum_j softmax_j(scale q_i.k_j + mask_ij) v_j.
 
     q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (any float dtype; upcast to float64).
     ``heads`` optionally restricts the work to a list of (b, h) pairs; the
-    other rows of the result are left as NaN.
+    other rows of the result are left as NaN.  ``window`` > 0 adds the
+    sliding window (causal only).
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
@@ -82,8 +98,38 @@ def attention(q, k, v, causal, scale, heads=None):
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
     for b, h in pairs:
         kh = h // G
-        p = _softmax_rows(_scores(q[b, :, h, :], k[b, :, kh, :], scale, causal))
+        p = _softmax_rows(_scores(q[b, :, h, :], k[b, :, kh, :], scale, causal, window))
         out[b, :, h, :] = p @ v[b, :, kh, :]
+    return out
+
+
+def attention_cache(q, k_cache, v_cache, kv_lens, causal, scale, window=0, heads=None):
+    """Chunked / variable-length prefill against a cache.
+
+    q [B,Sq,Hq,D]; caches [B,Hkv,max_kv,D] holding kv_len_b (clamped to
+    [0, max_kv]) rotated rows per sequence.  Query i of sequence b sits at
+    absolute position kv_len_b - Sq + i; with ``causal`` it sees keys
+    j <= that position (and, with ``window`` W > 0, j > position - W); rows
+    that see no key are zeros.  Sq = 1 is decode; Sq = kv_len is a plain
+    prefill.  Returns float64 [B,Sq,Hq,D]; rows of pairs not in ``heads`` are
+    NaN when ``heads`` is given.
+    """
+    q = np.asarray(q, dtype=np.float64)
+    B, Sq, Hq, D = q.shape
+    _, Hkv, max_kv, _ = k_cache.shape
+    G = Hq // Hkv
+    out = np.full((B, Sq, Hq, D), np.nan)
+    pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
+    for b, h in pairs:
+        L = int(min(max(int(kv_lens[b]), 0), max_kv))
+        kh = h // G
+        if L == 0:
+            out[b, :, h, :] = 0.0
+            continue
+        kk = np.asarray(k_cache[b, kh, :L, :], dtype=np.float64)
+        vv = np.asarray(v_cache[b, kh, :L, :], dtype=np.float64)
+        p = _softmax_rows(_scores(q[b, :, h, :], kk, scale, causal, window))
+        out[b, :, h, :] = p @ vv
     return out
 
 

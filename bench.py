@@ -14,8 +14,10 @@ Prints ONE JSON line.  `value` is the prefill attention throughput in TFLOP/s
 attn_prefill launch time measured with HIP events on the launch stream); the
 decode figure (GB/s of K/V bytes read, each row once per GQA group) rides in
 `decode`.  `roofline` is for the prefill kernel against the bf16 dense MFMA
-peak; `decode.roofline` against HBM.  `cpu_baseline` times the float64 oracle
-on a bounded sample on the host cores.
+peak; `decode.roofline` against HBM.  `chunked_prefill` and `sliding_window`
+time the two prefill extensions (attn_prefill_cache) separately, after the
+timed steps.  `cpu_baseline` times the float64 oracle on a bounded sample on
+the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
 """
@@ -81,6 +83,56 @@ def cpu_baseline(budget_s=12.0):
             "sample": f"{done} whole (batch, head) pairs of the B=2 S=4096 D=128 causal prefill "
                       f"(RoPE + attention, float64 numpy) in {dt:.1f} s; cpus visible "
                       f"{len(os.sched_getaffinity(0))}"}
+
+
+def _time_launches(fn, stream, warmup=20, reps=200):
+    """Mean time (ms) of one launch of fn, HIP events on the launch stream."""
+    import torch
+    for _ in range(warmup):
+        fn()
+    torch.cuda.synchronize()
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record(stream)
+    for _ in range(reps):
+        fn()
+    e1.record(stream)
+    torch.cuda.synchronize()
+    return e0.elapsed_time(e1) / reps
+
+
+def _next_rows(R, dev, stream):
+    """Throughput of the two prefill extensions on LLaMA-7B-shaped heads
+    (Hq = Hkv = 32, D = 128, bf16, causal), outside the timed step:
+    * chunked prefill: B=2, a chunk of 512 new tokens at the end of a
+      4608-token cache (kv_lens = 4608);
+    * sliding window: B=2, S=4096 prefill through the cache entry point with
+      window 1024.
+    Algorithmic flops = 4*D per visible (query, key) pair per head."""
+    import torch
+    D, H, B = 128, 32, 2
+    g = torch.Generator(device=dev)
+    g.manual_seed(2024)
+    out = {}
+    for name, Sq, L, window in (("chunked_prefill", 512, 4608, 0), ("sliding_window", 4096, 4096, 1024)):
+        q = torch.randn((B, Sq, H, D), generator=g, device=dev).to(torch.bfloat16)
+        kc = torch.randn((B, H, L, D), generator=g, device=dev).to(torch.bfloat16)
+        vc = torch.randn((B, H, L, D), generator=g, device=dev).to(torch.bfloat16)
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        pos = np.arange(Sq, dtype=np.int64) + (L - Sq)
+        seen = np.minimum(pos + 1, window) if window else pos + 1
+        flops = 4.0 * D * H * B * float(seen.sum())
+        ms = _time_launches(lambda: R.attn_prefill_cache(q, kc, vc, lens, o, causal=True, scale=D ** -0.5,
+                                                         window=window), stream)
+        tf = flops / (ms * 1e-3) / 1e12
+        out[name] = {"workload": f"B={B} Hq=Hkv={H} D={D} bf16 causal, Sq={Sq} new tokens, kv_len={L}"
+                                 + (f", window={window}" if window else ""),
+                     "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 4),
+                     "algorithmic_flops": flops,
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+        del q, kc, vc, o
+    return out
 
 
 def main():
@@ -186,6 +238,7 @@ def main():
     pre_tflops = pre_flops / (pre_ms.mean() * 1e-3) / 1e12
     dec_gbps = dec_bytes / (dec_ms.mean() * 1e-3) / 1e9
     rope_bytes = 2.0 * wp.B * wp.S * (wp.Hq + wp.Hkv) * wp.D * 2
+    extras = _next_rows(R, dev, stream)
     res = {
         "metric": METRIC,
         "value": round(pre_tflops, 2),
@@ -215,6 +268,8 @@ def main():
         "rope": {"value": round(rope_bytes / (rope_ms.mean() * 1e-3) / 1e9, 1), "unit": "GB/s",
                  "launch_ms": round(float(rope_ms.mean()), 4)},
         "hbm_copy_gbps": round(copy_gbps, 1),
+        "chunked_prefill": extras["chunked_prefill"],
+        "sliding_window": extras["sliding_window"],
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -5,11 +5,13 @@
  *
  * Sources (titles and sections of the pages the method is taken from):
  *   [HF]   "【HuggingFace Transformers】LlamaAttention源码解析" -- section 1.2 (attention
- *          steps 1-5), section 2 (LlamaAttention.forward, steps 1-6).
+ *          steps 1-5), section 2 (LlamaAttention.forward, steps 1-6), section 3.1
+ *          (LlamaFlashAttention2: variable lengths, mask alignment).
  *   [L2]   "LLaMA2大语言模型架构详解" -- sections "Rotary Position Encoding", "KV cache",
  *          "Grouped Multi-Query Attention (GQA)".
  *   [L2X]  "Llama2 Transformer架构解析与优化实践" -- sections 2.1, 3.2, 6.1.
- *   [VERL] "llama.py — LLaMA 注意力层 Ulysses SP 适配" -- "Ulysses SP 核心流程", step 2.
+ *   [VERL] "llama.py — LLaMA 注意力层 Ulysses SP 适配" -- "Ulysses SP 核心流程", step 2
+ *          ("第二步：RoPE + Flash Attention", including its sliding_window argument).
  *   [TP]   "LLM Lab 实验手记 05：注意力张量并行" -- sections 2 and 5.
  *
  * Conventions shared by every entry point:
@@ -101,6 +103,45 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
                           int B, int S, int Hq, int Hkv, int head_dim,
                           int causal, float scale,
                           rcgqa_dtype dt, rcgqa_stream stream);
+
+/*
+ * attn_prefill_cache -- chunked / variable-length prefill against a KV cache,
+ * with an optional causal sliding window.
+ *
+ * Defines: [HF] section 1.2 steps 2-4 and section 2 steps 4-5 (scores, mask,
+ * fp32 softmax, weights @ V, repeat_kv head map) for a block of Sq new query
+ * tokens per sequence whose keys and values, together with all earlier ones,
+ * are in the cache ([L2] "KV cache"; [HF] section 3.1: variable-length
+ * sequences, and the mask aligned to the end of the key range, the
+ * use_top_left_mask alternative being the other alignment).  The sliding
+ * window is the one the flash-attention call of [VERL] "第二步：RoPE + Flash
+ * Attention" passes; the pages do not define it, so the reading is: the
+ * query at absolute position p sees only keys p - window < j <= p.
+ *
+ *   L_b = clamp(kv_lens[b], 0, max_kv);  query i of sequence b is at p = L_b - Sq + i
+ *   out[b,i,h,:] = sum_{j in K(b,i)} softmax_j(scale * q[b,i,h,:].K[b,h/G,j,:]) V[b,h/G,j,:]
+ *   K(b,i) = { j < L_b }                                   causal == 0
+ *          = { j <= p }                                    causal == 1, window == 0
+ *          = { p - window < j <= p }                       causal == 1, window > 0
+ *   A row with an empty K(b,i) (p < 0, or L_b == 0) is a zero row.
+ *
+ * q        [B, Sq, Hq, head_dim]          (already rotated)
+ * k_cache  [B, Hkv, max_kv, head_dim]     rows 0..L_b-1 valid, already rotated;
+ *                                         the last Sq of them are this block's own keys
+ * v_cache  [B, Hkv, max_kv, head_dim]
+ * kv_lens  [B] int32 device array (not read on the host; clamped by the kernels)
+ * out      [B, Sq, Hq, head_dim]
+ * causal 0 or 1; window >= 0 (0 = none; window > 0 needs causal == 1).
+ * scale > 0, finite.  Hq % Hkv == 0.  head_dim: 64 or 128 (bf16 and fp32).
+ * Sq == 1 is a decode step (attn_decode is the faster kernel for it); Sq ==
+ * L_b for every b is a plain prefill.  Numerics as attn_prefill.  out must not
+ * alias q or the caches.
+ */
+rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* v_cache,
+                                const int32_t* kv_lens, void* out,
+                                int B, int Sq, int Hq, int Hkv, int head_dim, int max_kv,
+                                int causal, int window, float scale,
+                                rcgqa_dtype dt, rcgqa_stream stream);
 
 /*
  * attn_decode_workspace_bytes -- bytes of scratch attn_decode needs for these

@@ -40,6 +40,8 @@ def lib():
     L.rope_apply.restype = i32
     L.attn_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_prefill.restype = i32
+    L.attn_prefill_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.attn_prefill_cache.restype = i32
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -127,6 +129,29 @@ def attn_prefill(q, k, v, out=None, causal=True, scale=None):
                             _dev(out, "out", dt, 4), B, S, Hq, Hkv, D, int(bool(causal)),
                             float(scale), dt, _stream(q))
     _check(st, "attn_prefill")
+    return out
+
+
+def attn_prefill_cache(q, k_cache, v_cache, kv_lens, out=None, causal=True, scale=None, window=0):
+    """out [B,Sq,Hq,D] = attention of the Sq newest tokens q [B,Sq,Hq,D] of each
+    sequence over its kv_lens[b] cached rows (caches [B,Hkv,max_kv,D]); with
+    ``window`` > 0 a token sees only its ``window`` most recent positions."""
+    import torch
+    dt = _dtype_code(q)
+    B, Sq, Hq, D = q.shape
+    _, Hkv, max_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, max_kv, D) or tuple(v_cache.shape) != (B, Hkv, max_kv, D):
+        raise ValueError("caches must be [B, Hkv, max_kv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, Sq, Hq, D):
+        raise ValueError("out must be [B, Sq, Hq, D]")
+    scale = D ** -0.5 if scale is None else scale
+    st = lib().attn_prefill_cache(_dev(q, "q", dt, 4), _dev(k_cache, "k_cache", dt, 4),
+                                  _dev(v_cache, "v_cache", dt, 4), _i32(kv_lens, "kv_lens", B),
+                                  _dev(out, "out", dt, 4), B, Sq, Hq, Hkv, D, max_kv, int(bool(causal)),
+                                  int(window), float(scale), dt, _stream(q))
+    _check(st, "attn_prefill_cache")
     return out
 
 

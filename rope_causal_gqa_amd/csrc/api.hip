@@ -67,10 +67,35 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
   if (mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0) return RCGQA_EINVAL;
   if (!attn_head_dim(head_dim) || (S + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
+  // K/V in [B, S, Hkv, D]: every sequence has S keys, queries aligned with them
+  const rcgqa::KvSpec kv{(long long)S * Hkv * head_dim, head_dim, (long long)Hkv * head_dim, nullptr, S, 0};
   if (dt == RCGQA_BF16)
-    return hip_status(rcgqa::launch_prefill_bf16(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, st));
+    return hip_status(rcgqa::launch_prefill_bf16(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, kv, st));
   return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, B, S,
-                                              Hq, Hkv, head_dim, causal != 0, scale, st));
+                                              Hq, Hkv, head_dim, causal != 0, scale, kv, st));
+}
+
+rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_lens,
+                                void* out, int B, int Sq, int Hq, int Hkv, int head_dim, int max_kv, int causal,
+                                int window, float scale, rcgqa_dtype dt, rcgqa_stream stream) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !out || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (out == q || out == k_cache || out == v_cache) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(Sq) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv))
+    return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (window < 0 || (window > 0 && causal == 0)) return RCGQA_EINVAL;
+  if (mul({B, Hq}) > kI32Max || mul({B, Sq, Hq, head_dim}) < 0 || mul({B, Hkv, max_kv, head_dim}) < 0)
+    return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || (Sq + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  // caches [B, Hkv, max_kv, D]: rows of one (batch, KV head) are contiguous
+  const rcgqa::KvSpec kv{(long long)Hkv * max_kv * head_dim, (long long)max_kv * head_dim, head_dim, kv_lens,
+                         max_kv, window};
+  if (dt == RCGQA_BF16)
+    return hip_status(rcgqa::launch_prefill_bf16(q, k_cache, v_cache, out, B, Sq, Hq, Hkv, head_dim, causal != 0,
+                                                 scale, kv, st));
+  return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache,
+                                              (float*)out, B, Sq, Hq, Hkv, head_dim, causal != 0, scale, kv, st));
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv) {

@@ -7,14 +7,27 @@
 
 namespace rcgqa {
 
+// Where a prefill kernel finds the keys and values of (batch b, KV head g)
+// and how many there are.  Element strides: row j of (b, g) starts at
+// b*sb + g*sh + j*sr.  `lens` (device, may be null) holds each sequence's key
+// count, clamped to [0, max_kv]; null means Sk = Sq.  Query i of a sequence
+// with Sk keys sits at absolute position i + Sk - Sq; with a causal mask it
+// sees keys j <= that position and, when window > 0, only j > position - window.
+struct KvSpec {
+  long long sb, sh, sr;
+  const int32_t* lens;
+  int max_kv;
+  int window;
+};
+
 hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
                        double theta, double factor, bool bf16, hipStream_t st);
 
-hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* out, int B, int S,
-                              int Hq, int Hkv, int D, bool causal, float scale, hipStream_t st);
+hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* out, int B, int Sq,
+                              int Hq, int Hkv, int D, bool causal, float scale, const KvSpec& kv, hipStream_t st);
 
-hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int S,
-                               int Hq, int Hkv, int D, bool causal, float scale, hipStream_t st);
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int Sq,
+                               int Hq, int Hkv, int D, bool causal, float scale, const KvSpec& kv, hipStream_t st);
 
 // Split-K decode: partial softmax states go to `ws`, then a merge pass writes out.
 size_t decode_workspace_bytes(int B, int Hq, int D, int max_kv);

@@ -29,6 +29,10 @@
 //  * Causal: tiles past the block's last row are never loaded; a wave skips
 //    the math of tiles past its own last row; only diagonal / tail tiles pay
 //    for per-element masking.  Heaviest query tiles are dispatched first.
+//  * The same kernel serves chunked / variable-length prefill against a cache
+//    (keys through strides, per-sequence key counts, queries aligned to the
+//    end of their sequence) and the causal sliding window, whose tiles
+//    before the block's first window are never loaded either.
 #include <type_traits>
 
 #include "common.h"
@@ -48,11 +52,14 @@ __device__ __forceinline__ void lds_dma16(const void* g, bf16* l) {
   __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3)))*)(l), 16, 0, 0);
 }
 
-template <int D, int NW>
+// GEN: keys through per-sequence counts (query rows aligned to the end of
+// their sequence) and an optional sliding window; without it every sequence
+// has Sq keys, queries and keys aligned, and the bounds fold to constants.
+template <int D, int NW, bool GEN>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
-                                                             int S, int Hq, int Hkv, int causal, float c_log2,
-                                                             int nqt, int npairs) {
+                                                             int Sq, int Hq, int Hkv, int causal, float c_log2,
+                                                             int nqt, int npairs, KvSpec kv) {
   constexpr int BM = 32 * NW; // query rows per workgroup (32 per wave)
   constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the output head dim
@@ -82,17 +89,20 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int bh = item / npairs, slot = item - bh * npairs;
   const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / (Hq / Hkv);
-  const size_t qrs = (size_t)Hq * D, kvrs = (size_t)Hkv * D;
-  const bf16* kb = k + (size_t)b * S * kvrs + (size_t)kvh * D;
-  const bf16* vb = v + (size_t)b * S * kvrs + (size_t)kvh * D;
+  const size_t qrs = (size_t)Hq * D, kvrs = (size_t)kv.sr;
+  const bf16* kb = k + (size_t)b * kv.sb + (size_t)kvh * kv.sh;
+  const bf16* vb = v + (size_t)b * kv.sb + (size_t)kvh * kv.sh;
+  // this sequence's keys; query i sits at absolute position i + off
+  const int nkeys = GEN ? min(max(kv.lens[b], 0), kv.max_kv) : Sq;
+  const int off = GEN ? nkeys - Sq : 0, W = GEN ? kv.window : 0;
   const int qt_first = npairs < nqt ? nqt - 1 - slot : slot;
   const int npass = (npairs < nqt && slot != nqt - 1 - slot) ? 2 : 1;
   auto run_qtile = [&](const int q0) __attribute__((always_inline)) {
 
   const int qrow = q0 + w * 32 + col;  // this lane's query row
   bf16x8 qf[KS];
-  if (qrow < S) {
-    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)b * S + qrow) * qrs + (size_t)h * D);
+  if (qrow < Sq) {
+    const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)b * Sq + qrow) * qrs + (size_t)h * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) qf[ks] = src[2 * ks + hf];
   } else {
@@ -103,11 +113,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   // Tile loader: wave w fills tile rows [w BN/NW, (w+1) BN/NW) of K and V with
   // direct global->LDS loads.  Lane p of a load lands at physical chunk
   // p % CH of row p / CH, so it fetches the logical chunk that the swizzle
-  // puts there.  Keys past S are clamped to S-1 (finite data; masked later).
+  // puts there.  Keys past Sk are clamped to Sk-1 (finite data; masked later).
   const int lrow = lane / CH, lpc = lane % CH;
   // Byte offsets of this lane's loads inside a tile do not depend on the tile:
   // computed once (32-bit), so a full tile costs one scalar base update and no
-  // per-lane address arithmetic.  Only a tile crossing S clamps per lane.
+  // per-lane address arithmetic.  Only a tile crossing Sk clamps per lane.
   uint32_t loff[LD_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LD_PER_WAVE; i++) {
@@ -117,7 +127,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   auto issue = [&](int t, int buf)  __attribute__((always_inline)) {
     bf16* kd = lds + buf * 2 * TILE;
     bf16* vd = kd + TILE;
-    if (t * BN + BN <= S) {
+    if (t * BN + BN <= nkeys) {
       const char* kt = reinterpret_cast<const char*>(kb + (size_t)t * BN * kvrs);
       const char* vt = reinterpret_cast<const char*>(vb + (size_t)t * BN * kvrs);
 #pragma unroll
@@ -131,7 +141,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       for (int i = 0; i < LD_PER_WAVE; i++) {
         const int r0 = wu * (BN / NW) + i * ROWS_PER_LD;
         const int r = r0 + lrow;
-        const int key = min(t * BN + r, S - 1);
+        const int key = min(t * BN + r, nkeys - 1);
         const size_t goff = (size_t)key * kvrs + (size_t)((lpc ^ (row_swizzle(r) & SW)) << 3);
         lds_dma16(kb + goff, kd + r0 * D);
         lds_dma16(vb + goff, vd + r0 * D);
@@ -142,10 +152,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; db++) o[db] = f32x16{};
-  float m_run = -INFINITY, l_run = 0.f;
+  // A finite start for the running max: a row whose first tiles are fully
+  // masked (sliding window) then keeps zero weights instead of exp2(-inf + inf).
+  float m_run = -1e30f, l_run = 0.f;
 
-  const int kv_end = causal ? min(S, q0 + BM) : S;
-  const int ntiles = (kv_end + BN - 1) / BN;
+  // keys any row of this query tile can see: tiles [t_lo, t_hi)
+  const int key_hi = causal ? min(nkeys, q0 + BM + off) : nkeys;
+  const int key_lo = (causal && W > 0) ? max(0, q0 + off - W + 1) : 0;
+  const int t_lo = key_lo / BN, t_hi = key_hi > 0 ? (key_hi + BN - 1) / BN : 0;
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
 
   // transpose-read addressing of V (fixed per lane)
@@ -173,8 +187,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   auto tile_step = [&](int t, auto bufc)  __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const int kv0 = t * BN;
-    if (t + 1 < ntiles) issue(t + 1, buf ^ 1);
-    if (!(causal && kv0 > wrow_hi)) {  // else the whole tile is masked for this wave
+    if (t + 1 < t_hi) issue(t + 1, buf ^ 1);
+    // else the whole tile is masked for this wave (past its last row, or before its window)
+    if (!(causal && kv0 > wrow_hi + off) && !(W > 0 && kv0 + BN - 1 <= wrow_lo + off - W)) {
       const bf16* sk = lds + buf * 2 * TILE;
       const bf16* sv = sk + TILE;
 
@@ -200,13 +215,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       }
 
       // mask (diagonal / tail tiles only) and row max on raw scores
-      if ((causal && kv0 + BN - 1 > wrow_lo) || kv0 + BN > S) {
+      if ((causal && kv0 + BN - 1 > wrow_lo + off) || kv0 + BN > nkeys || (W > 0 && kv0 <= wrow_hi + off - W)) {
 #pragma unroll
         for (int kb2 = 0; kb2 < 2; kb2++)
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             const int key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (key >= S || (causal && key > qrow)) s[kb2][i] = -INFINITY;
+            if (key >= nkeys || (causal && key > qrow + off) || (W > 0 && key <= qrow + off - W)) s[kb2][i] = -INFINITY;
           }
       }
       float mx = s[0][0];
@@ -256,18 +271,18 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
     __syncthreads();                // ... and everyone's; tile t fully consumed
   };
-  issue(0, 0);
+  if (t_lo < t_hi) issue(t_lo, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = 0; t < ntiles; t += 2) {
+  for (int t = t_lo; t < t_hi; t += 2) {
     tile_step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < ntiles) tile_step(t + 1, std::integral_constant<int, 1>{});
+    if (t + 1 < t_hi) tile_step(t + 1, std::integral_constant<int, 1>{});
   }
 
   const float l_tot = half_swap_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < S) {
-    bf16* dst = out + ((size_t)b * S + qrow) * qrs + (size_t)h * D;
+  if (qrow < Sq) {
+    bf16* dst = out + ((size_t)b * Sq + qrow) * qrs + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; db++) {
 #pragma unroll
@@ -285,21 +300,30 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   if (npass == 2) run_qtile(slot * BM);
 }
 
-template <int NW>
-static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq, int Hkv,
-                      int D, bool causal, float c_log2, int npairs, hipStream_t st) {
-  const int nqt = (S + 32 * NW - 1) / (32 * NW);
+template <int NW, bool GEN>
+static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
+                      int D, bool causal, float c_log2, int npairs, const KvSpec& kv, hipStream_t st) {
+  const int nqt = (Sq + 32 * NW - 1) / (32 * NW);
   const dim3 grid((unsigned)((long long)B * Hq * npairs)), block(64 * NW);
   if (D == 64)
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2, nqt, npairs);
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW, GEN>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (bf16*)out, S, Hq, Hkv, (int)causal, c_log2, nqt, npairs);
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW, GEN>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
+                       (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
 }
 
-hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq,
-                               int Hkv, int D, bool causal, float scale, hipStream_t st) {
+template <int NW>
+static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
+                      int D, bool causal, float c_log2, int npairs, const KvSpec& kv, hipStream_t st) {
+  if (kv.lens || kv.window > 0)
+    launch_nw<NW, true>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+  else
+    launch_nw<NW, false>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+}
+
+hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
+                               int Hkv, int D, bool causal, float scale, const KvSpec& kv, hipStream_t st) {
   const float c_log2 = (float)((double)scale * 1.4426950408889634);
   // Every K/V tile brought into LDS serves the workgroup's query rows, so 8
   // waves (256 rows) halve the tile traffic per flop against 4 waves (128
@@ -309,12 +333,12 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   // workgroups or more, otherwise 4 waves keep more CUs busy, pairing only
   // when 512 paired workgroups result.
   const long long bh = (long long)B * Hq;
-  const int nqt8 = (S + 255) / 256, nqt4 = (S + 127) / 128;
+  const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
   if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512) {
-    launch_nw<8>(q, k, v, out, B, S, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, st);
+    launch_nw<8>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, kv, st);
   } else {
     const int npairs = (causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512) ? (nqt4 + 1) / 2 : nqt4;
-    launch_nw<4>(q, k, v, out, B, S, Hq, Hkv, D, causal, c_log2, npairs, st);
+    launch_nw<4>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
   }
   return hipGetLastError();
 }

@@ -23,8 +23,8 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert set(names) >= {"rope_apply", "attn_prefill", "attn_decode", "attn_decode_workspace_bytes",
-                          "kv_append", "rcgqa_status_string"}
+    assert set(names) >= {"rope_apply", "attn_prefill", "attn_prefill_cache", "attn_decode",
+                          "attn_decode_workspace_bytes", "kv_append", "rcgqa_status_string"}
     L = R.lib()
     for n in names:
         assert hasattr(L, n), n
@@ -92,6 +92,26 @@ def test_prefill_unsupported_head_dim(D):
 
 
 @pytest.mark.parametrize("args", [
+    dict(out=None), dict(same=True), dict(lens=None), dict(B=0), dict(Sq=0), dict(Hq=6, Hkv=4),
+    dict(max_kv=0), dict(D=5), dict(causal=3), dict(window=-1), dict(window=8, causal=0), dict(scale=0.0),
+    dict(scale=float("inf")), dict(dt=5),
+])
+def test_prefill_cache_rejects(args):
+    a = dict(q=FAKE, out=ctypes.c_void_p(8192), lens=FAKE, B=2, Sq=16, Hq=8, Hkv=2, D=128, max_kv=100, causal=1,
+             window=0, scale=0.1, dt=0)
+    a.update(args)
+    out = a["q"] if a.get("same") else a["out"]
+    st = R.lib().attn_prefill_cache(a["q"], FAKE, FAKE, a["lens"], out, a["B"], a["Sq"], a["Hq"], a["Hkv"], a["D"],
+                                    a["max_kv"], a["causal"], a["window"], a["scale"], a["dt"], None)
+    assert st == BD.EINVAL
+
+
+def test_prefill_cache_unsupported_head_dim():
+    assert R.lib().attn_prefill_cache(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(8192), 1, 4, 8, 2, 96, 10, 1, 0, 0.1,
+                                      0, None) == BD.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("args", [
     dict(ws=None), dict(wbytes=0), dict(ws_addr=4096 + 8), dict(Hq=12, Hkv=8), dict(max_kv=0), dict(scale=-1.0),
     dict(lens=None),
 ])
@@ -124,3 +144,5 @@ def test_binding_requires_device_tensors():
         R.rope_apply(q, q.clone())
     with pytest.raises(ValueError):
         R.attn_prefill(q, q, q)
+    with pytest.raises(ValueError):
+        R.attn_prefill_cache(q, q, q, torch.zeros(1, dtype=torch.int32))

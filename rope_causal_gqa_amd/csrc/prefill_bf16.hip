@@ -52,6 +52,18 @@ __device__ __forceinline__ void lds_dma16(const void* g, bf16* l) {
   __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3)))*)(l), 16, 0, 0);
 }
 
+// The same 16-byte-per-lane direct load through a buffer descriptor: the
+// tile's base lives in scalar registers and the per-lane byte offset `voff`
+// is fixed for the whole kernel, so issuing a tile takes no vector address
+// arithmetic.  The descriptor is raw (unstrided) with the largest range: every
+// offset used is inside the tensor by construction.  The last word is the
+// gfx9-family buffer format for untyped dword access.
+__device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16* l) {
+  const __amdgpu_buffer_rsrc_t rs =
+      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3)))*)(l), 16, voff, 0, 0, 0);
+}
+
 // GEN: keys through per-sequence counts (query rows aligned to the end of
 // their sequence) and an optional sliding window; without it every sequence
 // has Sq keys, queries and keys aligned, and the bounds fold to constants.
@@ -128,13 +140,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     bf16* kd = lds + buf * 2 * TILE;
     bf16* vd = kd + TILE;
     if (t * BN + BN <= nkeys) {
-      const char* kt = reinterpret_cast<const char*>(kb + (size_t)t * BN * kvrs);
-      const char* vt = reinterpret_cast<const char*>(vb + (size_t)t * BN * kvrs);
+      const bf16* kt = kb + (size_t)t * BN * kvrs;
+      const bf16* vt = vb + (size_t)t * BN * kvrs;
 #pragma unroll
       for (int i = 0; i < LD_PER_WAVE; i++) {
         const int r0 = wu * (BN / NW) + i * ROWS_PER_LD;  // wave-uniform
-        lds_dma16(kt + loff[i], kd + r0 * D);
-        lds_dma16(vt + loff[i], vd + r0 * D);
+        lds_buf16(kt, loff[i], kd + r0 * D);
+        lds_buf16(vt, loff[i], vd + r0 * D);
       }
     } else {
 #pragma unroll
@@ -154,13 +166,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   for (int db = 0; db < DB; db++) o[db] = f32x16{};
   // A finite start for the running max: a row whose first tiles are fully
   // masked (sliding window) then keeps zero weights instead of exp2(-inf + inf).
+  // m_lim = m_run + the lazy-rescale margin; nmc = -m_run * c_log2 (the exp offset).
   float m_run = -1e30f, l_run = 0.f;
+  float m_lim = m_run, nmc = -m_run * c_log2;
 
   // keys any row of this query tile can see: tiles [t_lo, t_hi)
   const int key_hi = causal ? min(nkeys, q0 + BM + off) : nkeys;
   const int key_lo = (causal && W > 0) ? max(0, q0 + off - W + 1) : 0;
   const int t_lo = key_lo / BN, t_hi = key_hi > 0 ? (key_hi + BN - 1) / BN : 0;
   const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
+  const float rescale_margin = kRescaleLog2 / c_log2;  // the lazy-rescale threshold in score units
 
   // transpose-read addressing of V (fixed per lane)
   const int r16 = lane & 15, g = lane >> 4;
@@ -233,28 +248,33 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
 
       // lazy rescale: move the reference max only when some row grew by more
       // than 2^kRescaleLog2 (exact either way: O and l share the reference)
-      const float m_new = fmaxf(m_run, mx);
-      if (__any((m_new - m_run) * c_log2 > kRescaleLog2)) {
+      if (__any(mx > m_lim)) {
+        const float m_new = fmaxf(m_run, mx);
         const float alpha = fast_exp2((m_run - m_new) * c_log2);
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; db++) o[db] *= alpha;
         m_run = m_new;
+        m_lim = m_new + rescale_margin;
+        nmc = -m_new * c_log2;
       }
-      const float mc = m_run * c_log2;
       bf16x8 pf[4];
 #pragma unroll
       for (int kb2 = 0; kb2 < 2; kb2++) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)fast_exp2(fmaf(s[kb2][i], c_log2, -mc));
+        for (int i = 0; i < 16; i++) pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)fast_exp2(fmaf(s[kb2][i], c_log2, nmc));
       }
-      // row sum of the bf16 weights actually fed to the MFMA (two per dot2)
-      float ps[4] = {0.f, 0.f, 0.f, 0.f};
+      // row sum of the bf16 weights actually fed to the MFMA (two per dot2,
+      // two chains, one of them continuing the running sum)
+      float sa = l_run, sb = 0.f;
 #pragma unroll
       for (int j = 0; j < 4; j++)
 #pragma unroll
-        for (int e = 0; e < 4; e++) ps[e] = bf16_pair_sum(pf[j][2 * e], pf[j][2 * e + 1], ps[e]);
-      l_run += (ps[0] + ps[1]) + (ps[2] + ps[3]);
+        for (int e = 0; e < 4; e += 2) {
+          sa = bf16_pair_sum(pf[j][2 * e], pf[j][2 * e + 1], sa);
+          sb = bf16_pair_sum(pf[j][2 * e + 2], pf[j][2 * e + 3], sb);
+        }
+      l_run = sa + sb;
 
       // O^T += V^T P^T over four 16-key chunks
 #pragma unroll

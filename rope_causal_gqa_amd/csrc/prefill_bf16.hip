@@ -67,12 +67,17 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
 // GEN: keys through per-sequence counts (query rows aligned to the end of
 // their sequence) and an optional sliding window; without it every sequence
 // has Sq keys, queries and keys aligned, and the bounds fold to constants.
-template <int D, int NW, bool GEN>
+// KSPLIT = 2: the NW waves form two groups that take the same 32*NW/2 query
+// rows over the two halves of the key range, each with its own LDS tiles, and
+// merge their softmax states through LDS at the end (more waves in flight for
+// grids too small to fill the GPU, with no memory outside the workgroup).
+template <int D, int NW, bool GEN, int KSPLIT>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
                                                              int Sq, int Hq, int Hkv, int causal, float c_log2,
                                                              int nqt, int npairs, KvSpec kv) {
-  constexpr int BM = 32 * NW; // query rows per workgroup (32 per wave)
+  constexpr int NWG = NW / KSPLIT;  // waves per key group
+  constexpr int BM = 32 * NWG;      // query rows per workgroup (32 per wave of a group)
   constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
   constexpr int DB = D / 32;  // 32-wide blocks of the output head dim
   constexpr int CH = D / 8;   // 16-byte chunks per row
@@ -80,12 +85,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   static_assert(CH <= 16 && (CH & (CH - 1)) == 0, "D must be 64 or 128");
   constexpr int TILE = BN * D;              // elements of one K (or V) tile
   constexpr int ROWS_PER_LD = 64 / CH;      // rows one wave-wide 16-byte load fills
-  constexpr int LD_PER_WAVE = BN / NW / ROWS_PER_LD;
+  constexpr int LD_PER_WAVE = BN / NWG / ROWS_PER_LD;
   static_assert(LD_PER_WAVE >= 1, "tile rows per wave");
-  __shared__ __attribute__((aligned(16))) bf16 lds[2 * 2 * TILE];  // [buffer][K | V][BN][D]
+  __shared__ __attribute__((aligned(16))) bf16 lds[KSPLIT * 2 * 2 * TILE];  // [group][buffer][K | V][BN][D]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
+  const int grp = KSPLIT > 1 ? wu / NWG : 0, wr = KSPLIT > 1 ? wu % NWG : wu;  // key group; rows slot
+  bf16* const ldsg = lds + grp * 2 * 2 * TILE;
   const int col = lane & 31, hf = lane >> 5;
   // Work item of this workgroup.  The work list is ordered (batch, query head,
   // query-tile slot), so consecutive items share a head and consecutive heads
@@ -111,7 +118,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int npass = (npairs < nqt && slot != nqt - 1 - slot) ? 2 : 1;
   auto run_qtile = [&](const int q0) __attribute__((always_inline)) {
 
-  const int qrow = q0 + w * 32 + col;  // this lane's query row
+  const int qrow = q0 + wr * 32 + col;  // this lane's query row
   bf16x8 qf[KS];
   if (qrow < Sq) {
     const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)b * Sq + qrow) * qrs + (size_t)h * D);
@@ -122,7 +129,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     for (int ks = 0; ks < KS; ks++) qf[ks] = bf16x8{};
   }
 
-  // Tile loader: wave w fills tile rows [w BN/NW, (w+1) BN/NW) of K and V with
+  // Tile loader: wave wr of a group fills tile rows [wr BN/NWG, (wr+1) BN/NWG) of K and V with
   // direct global->LDS loads.  Lane p of a load lands at physical chunk
   // p % CH of row p / CH, so it fetches the logical chunk that the swizzle
   // puts there.  Keys past Sk are clamped to Sk-1 (finite data; masked later).
@@ -133,25 +140,25 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   uint32_t loff[LD_PER_WAVE];
 #pragma unroll
   for (int i = 0; i < LD_PER_WAVE; i++) {
-    const int r = wu * (BN / NW) + i * ROWS_PER_LD + lrow;
+    const int r = wr * (BN / NWG) + i * ROWS_PER_LD + lrow;
     loff[i] = (uint32_t)(r * (int)kvrs + ((lpc ^ (row_swizzle(r) & SW)) << 3)) * (uint32_t)sizeof(bf16);
   }
   auto issue = [&](int t, int buf)  __attribute__((always_inline)) {
-    bf16* kd = lds + buf * 2 * TILE;
+    bf16* kd = ldsg + buf * 2 * TILE;
     bf16* vd = kd + TILE;
     if (t * BN + BN <= nkeys) {
       const bf16* kt = kb + (size_t)t * BN * kvrs;
       const bf16* vt = vb + (size_t)t * BN * kvrs;
 #pragma unroll
       for (int i = 0; i < LD_PER_WAVE; i++) {
-        const int r0 = wu * (BN / NW) + i * ROWS_PER_LD;  // wave-uniform
+        const int r0 = wr * (BN / NWG) + i * ROWS_PER_LD;  // wave-uniform
         lds_buf16(kt, loff[i], kd + r0 * D);
         lds_buf16(vt, loff[i], vd + r0 * D);
       }
     } else {
 #pragma unroll
       for (int i = 0; i < LD_PER_WAVE; i++) {
-        const int r0 = wu * (BN / NW) + i * ROWS_PER_LD;
+        const int r0 = wr * (BN / NWG) + i * ROWS_PER_LD;
         const int r = r0 + lrow;
         const int key = min(t * BN + r, nkeys - 1);
         const size_t goff = (size_t)key * kvrs + (size_t)((lpc ^ (row_swizzle(r) & SW)) << 3);
@@ -174,7 +181,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int key_hi = causal ? min(nkeys, q0 + BM + off) : nkeys;
   const int key_lo = (causal && W > 0) ? max(0, q0 + off - W + 1) : 0;
   const int t_lo = key_lo / BN, t_hi = key_hi > 0 ? (key_hi + BN - 1) / BN : 0;
-  const int wrow_lo = q0 + w * 32, wrow_hi = wrow_lo + 31;
+  // this group's tiles [tg_lo, tg_hi); both groups run `steps` barrier steps
+  const int ntl = max(t_hi - t_lo, 0), steps = (ntl + KSPLIT - 1) / KSPLIT;
+  const int tg_lo = t_lo + grp * steps, tg_hi = min(tg_lo + steps, t_lo + ntl);
+  const int wrow_lo = q0 + wr * 32, wrow_hi = wrow_lo + 31;
   const float rescale_margin = kRescaleLog2 / c_log2;  // the lazy-rescale threshold in score units
 
   // transpose-read addressing of V (fixed per lane)
@@ -202,10 +212,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   auto tile_step = [&](int t, auto bufc)  __attribute__((always_inline)) {
     constexpr int buf = decltype(bufc)::value;
     const int kv0 = t * BN;
-    if (t + 1 < t_hi) issue(t + 1, buf ^ 1);
-    // else the whole tile is masked for this wave (past its last row, or before its window)
-    if (!(causal && kv0 > wrow_hi + off) && !(W > 0 && kv0 + BN - 1 <= wrow_lo + off - W)) {
-      const bf16* sk = lds + buf * 2 * TILE;
+    if (t + 1 < tg_hi) issue(t + 1, buf ^ 1);
+    // else the whole tile is masked for this wave (past its last row, or before its window),
+    // or (second key group, odd tile count) past the group's range
+    if (t < tg_hi && !(causal && kv0 > wrow_hi + off) && !(W > 0 && kv0 + BN - 1 <= wrow_lo + off - W)) {
+      const bf16* sk = ldsg + buf * 2 * TILE;
       const bf16* sv = sk + TILE;
 
       // S^T = K Q^T: two 32-key blocks, chains interleaved
@@ -291,17 +302,44 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     __builtin_amdgcn_s_waitcnt(0);  // this wave's loads of tile t+1 have landed
     __syncthreads();                // ... and everyone's; tile t fully consumed
   };
-  if (t_lo < t_hi) issue(t_lo, 0);
+  if (tg_lo < tg_hi) issue(tg_lo, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
-  for (int t = t_lo; t < t_hi; t += 2) {
-    tile_step(t, std::integral_constant<int, 0>{});
-    if (t + 1 < t_hi) tile_step(t + 1, std::integral_constant<int, 1>{});
+  for (int i = 0; i < steps; i += 2) {
+    tile_step(tg_lo + i, std::integral_constant<int, 0>{});
+    if (i + 1 < steps) tile_step(tg_lo + i + 1, std::integral_constant<int, 1>{});
+  }
+  if constexpr (KSPLIT == 2) {
+    // The second key group hands its state to its partner wave (same rows,
+    // same lane layout) through LDS; every tile is consumed and no load is in
+    // flight since the last step's barrier.
+    constexpr int NV = DB * 16 + 2;
+    float* xfer = reinterpret_cast<float*>(lds) + (size_t)wr * NV * 64 + lane;
+    if (grp == 1) {
+#pragma unroll
+      for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) xfer[(db * 16 + i) * 64] = o[db][i];
+      xfer[(DB * 16) * 64] = m_run;
+      xfer[(DB * 16 + 1) * 64] = l_run;
+    }
+    __syncthreads();
+    if (grp == 0) {
+      const float m1 = xfer[(DB * 16) * 64], l1 = xfer[(DB * 16 + 1) * 64];
+      const float m = fmaxf(m_run, m1);
+      const float a0 = fast_exp2((m_run - m) * c_log2), a1 = fast_exp2((m1 - m) * c_log2);
+      l_run = l_run * a0 + l1 * a1;
+#pragma unroll
+      for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) o[db][i] = o[db][i] * a0 + xfer[(db * 16 + i) * 64] * a1;
+    }
+    __syncthreads();  // the hand-over area is free again before any later tile load
   }
 
   const float l_tot = half_swap_sum(l_run);
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
-  if (qrow < Sq) {
+  if (grp == 0 && qrow < Sq) {
     bf16* dst = out + ((size_t)b * Sq + qrow) * qrs + (size_t)h * D;
 #pragma unroll
     for (int db = 0; db < DB; db++) {
@@ -320,26 +358,27 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   if (npass == 2) run_qtile(slot * BM);
 }
 
-template <int NW, bool GEN>
+template <int NW, bool GEN, int KSPLIT>
 static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
                       int D, bool causal, float c_log2, int npairs, const KvSpec& kv, hipStream_t st) {
-  const int nqt = (Sq + 32 * NW - 1) / (32 * NW);
+  constexpr int BM = 32 * NW / KSPLIT;
+  const int nqt = (Sq + BM - 1) / BM;
   const dim3 grid((unsigned)((long long)B * Hq * npairs)), block(64 * NW);
   if (D == 64)
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW, GEN>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW, GEN, KSPLIT>), grid, block, 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW, GEN>), grid, block, 0, st, (const bf16*)q, (const bf16*)k,
-                       (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW, GEN, KSPLIT>), grid, block, 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
 }
 
-template <int NW>
+template <int NW, int KSPLIT>
 static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
                       int D, bool causal, float c_log2, int npairs, const KvSpec& kv, hipStream_t st) {
   if (kv.lens || kv.window > 0)
-    launch_nw<NW, true>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+    launch_nw<NW, true, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
   else
-    launch_nw<NW, false>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+    launch_nw<NW, false, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
@@ -349,16 +388,21 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   // waves (256 rows) halve the tile traffic per flop against 4 waves (128
   // rows).  Both run 8 waves per CU (one 8-wave or two 4-wave workgroups).
   // Causal grids pair heavy and light query tiles so all workgroups do equal
-  // work; 8 waves are used only when that paired grid still has 512
-  // workgroups or more, otherwise 4 waves keep more CUs busy, pairing only
-  // when 512 paired workgroups result.
+  // work.  In order of preference: 8 waves when that paired grid still has
+  // 512 workgroups or more; 4 waves when their grid (paired if that keeps 512
+  // workgroups) has 512 or more; otherwise 8 waves in two key groups over
+  // 128-row tiles, so a grid of fewer workgroups still runs 8 waves per CU.
   const long long bh = (long long)B * Hq;
   const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
   if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512) {
-    launch_nw<8>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, kv, st);
+    launch_nw<8, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, kv, st);
   } else {
-    const int npairs = (causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512) ? (nqt4 + 1) / 2 : nqt4;
-    launch_nw<4>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+    const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;
+    const int npairs = pair4 ? (nqt4 + 1) / 2 : nqt4;
+    if (bh * npairs >= 512)
+      launch_nw<4, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+    else
+      launch_nw<8, 2>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, nqt4, kv, st);
   }
   return hipGetLastError();
 }

@@ -121,3 +121,28 @@ def test_kv_append_rows():
     torch.cuda.synchronize()
     rk, rv = oracle.kv_append(host64(k0), host64(v0), host64(kn), host64(vn), slots)
     assert np.array_equal(host64(kc), rk) and np.array_equal(host64(vc), rv)
+
+
+@pytest.mark.parametrize("dtype", ["bf16", "fp32"])
+def test_decode_growing_scores(dtype):
+    """Cache keys whose scores grow with their position: every split of the
+    split-K pass (and the merge) sees maxima far apart."""
+    import torch
+    announce(f"decode growing scores {dtype}")
+    B, Hq, Hkv, D, max_kv = 3, 16, 2, 128, 5000
+    r = np.random.Generator(np.random.PCG64(404))
+    u = r.standard_normal(D)
+    u /= np.linalg.norm(u)
+    # fp32 keeps scores within ~20 so its rounding (proportional to |score|) stays under 1e-5
+    q = (30.0 if dtype == "bf16" else 10.0) * u + 0.3 * r.standard_normal((B, Hq, D))
+    kc = (np.arange(max_kv) / (200.0 if dtype == "bf16" else 400.0))[None, None, :, None] * u + 0.3 * r.standard_normal((B, Hkv, max_kv, D))
+    vc = r.standard_normal((B, Hkv, max_kv, D))
+    lens = np.array([4999, 2500, 700])
+    if dtype == "bf16":
+        q, kc, vc = (W.round_bf16(a) for a in (q, kc, vc))
+    else:
+        q, kc, vc = (a.astype(np.float32) for a in (q, kc, vc))
+    out = R.attn_decode(dev(q, dtype), dev(kc, dtype), dev(vc, dtype), _i32(lens), scale=D ** -0.5)
+    torch.cuda.synchronize()
+    ref = oracle.decode(W.to_f64(q, dtype), W.to_f64(kc, dtype), W.to_f64(vc, dtype), lens, D ** -0.5)
+    check(host64(out), ref, dtype, f"decode growing scores {dtype}")

@@ -162,3 +162,34 @@ def test_prefill_on_side_stream():
         out = R.attn_prefill(q, k, v, causal=False, scale=w.scale)
     torch.cuda.synchronize()
     assert torch.equal(out, ref)
+
+
+@pytest.mark.parametrize("dtype,S,D", [("bf16", 1000, 128), ("bf16", 700, 64), ("fp32", 300, 64)])
+def test_prefill_growing_scores(dtype, S, D):
+    """Scores that grow along the sequence move the running max by far more
+    than the lazy-rescale margin on almost every key tile, so the rescale of
+    the accumulators (rare on N(0,1) inputs) runs throughout."""
+    import torch
+    announce(f"prefill growing scores {dtype} S={S} D={D}")
+    r = np.random.Generator(np.random.PCG64(S + D))
+    u = r.standard_normal(D)
+    u /= np.linalg.norm(u)
+    B, Hq, Hkv = 1, 4, 2
+    # bf16: score growth per 64-key tile ~ 30 * 64/12 * scale = 14-20 (natural log
+    # units), well past the lazy-rescale margin of 2^8.  fp32 (no lazy rescale; it
+    # moves its max on every larger score) uses amplitude 10 so scores stay within
+    # ~40, where fp32 score rounding (proportional to |score|) keeps the 1e-5 bar.
+    amp = 30.0 if dtype == "bf16" else 10.0
+    q = (amp * u + 0.3 * r.standard_normal((B, S, Hq, D)))
+    ramp = (np.arange(S) / 12.0)[None, :, None, None]
+    k = ramp * u + 0.3 * r.standard_normal((B, S, Hkv, D))
+    v = r.standard_normal((B, S, Hkv, D))
+    if dtype == "bf16":
+        q, k, v = (W.round_bf16(a) for a in (q, k, v))
+    else:
+        q, k, v = (a.astype(np.float32) for a in (q, k, v))
+    scale = 1.0 / math.sqrt(D)
+    out = R.attn_prefill(dev(q, dtype), dev(k, dtype), dev(v, dtype), causal=True, scale=scale)
+    torch.cuda.synchronize()
+    ref = oracle.attention(W.to_f64(q, dtype), W.to_f64(k, dtype), W.to_f64(v, dtype), True, scale)
+    check(host64(out), ref, dtype, f"growing scores {dtype} S={S} D={D}")

@@ -195,6 +195,92 @@ rcgqa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const vo
                        const int32_t* slots, int B, int Hkv, int head_dim, int max_kv,
                        rcgqa_dtype dt, rcgqa_stream stream);
 
+/*
+ * rope_attn_prefill_workspace_bytes -- bytes of scratch rope_attn_prefill
+ * needs: one fp32 cos/sin row per token, B * S * head_dim * 4.  Pure host
+ * function; 0 if an argument is not positive or the size overflows.
+ */
+size_t rope_attn_prefill_workspace_bytes(int B, int S, int head_dim);
+
+/*
+ * rope_attn_prefill -- rope_apply followed by attn_prefill, with the query
+ * rotation done inside the attention kernel as each query row is loaded.
+ *
+ * Defines: the composition of rope_apply and attn_prefill above ([L2]
+ * "Rotary Position Encoding"; [HF] section 2 steps 3-5: rotate Q and K, then
+ * attention; [L2X] section 6.1 for linear_factor).  The result is the one the
+ * two separate calls produce, bit for bit: the keys are rotated by the same
+ * kernel, and each query row is rotated with the same fp32 cos/sin values and
+ * the same arithmetic and rounding before it enters the score products.
+ *
+ * q            [B, S, Hq,  head_dim]  read only: NOT rotated in memory
+ * k            [B, S, Hkv, head_dim]  in/out: rotated in place, as rope_apply
+ *                                     leaves it (the keys a KV cache keeps)
+ * v            [B, S, Hkv, head_dim]
+ * out          [B, S, Hq,  head_dim]
+ * position_ids [B, S] int32 device array, or NULL for 0..S-1 in every sequence.
+ * causal, scale, theta, linear_factor, Hq % Hkv, head_dim (64 or 128): as
+ * rope_apply and attn_prefill.
+ * workspace  device buffer of at least rope_attn_prefill_workspace_bytes(B, S,
+ *            head_dim) bytes, 256-byte aligned, owned by the caller; no initial
+ *            contents are required; it holds the cos/sin rows and concurrent
+ *            calls must not share it.
+ * out must not alias q, k or v, and q, k, v must be distinct buffers.
+ * Traffic: the rotation adds one read and one write of K (plus the small
+ * table) to the attention pass, instead of a read and write of Q and K.
+ */
+rcgqa_status rope_attn_prefill(const void* q, void* k, const void* v, void* out,
+                               const int32_t* position_ids,
+                               int B, int S, int Hq, int Hkv, int head_dim,
+                               int causal, float scale, float theta, float linear_factor,
+                               rcgqa_dtype dt, void* workspace, size_t workspace_bytes,
+                               rcgqa_stream stream);
+
+/*
+ * rope_attn_decode_workspace_bytes -- bytes of scratch rope_attn_decode needs
+ * (the rotated queries, then attn_decode's split-K partial states).  Pure host
+ * function; 0 if an argument is not positive.
+ */
+size_t rope_attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv);
+
+/*
+ * rope_attn_decode -- one decode step with the rotations and the cache append
+ * fused into one kernel ahead of the decode attention.
+ *
+ * Defines: [L2] "KV cache" (the new token's key and value are appended, its
+ * query attends to every cached key and itself) and "Rotary Position
+ * Encoding"; [HF] section 2 steps 3-5 (q and the new key are rotated at the
+ * token's position before the key is cached and attention runs).  Exactly
+ * the composition, bit for bit:
+ *   rope_apply(q, k_new at positions pos_b);
+ *   kv_append(k_cache, v_cache, rotated k_new, v_new, slots = kv_lens - 1);
+ *   attn_decode(rotated q, k_cache, v_cache, kv_lens, out)
+ * with pos_b = position_ids[b], or kv_lens[b] - 1 when position_ids is NULL
+ * (the new token sits right after the ctx = kv_lens[b] - 1 cached ones).
+ *
+ * q            [B, Hq, head_dim]   read only (not rotated in memory)
+ * k_new, v_new [B, Hkv, head_dim]  read only
+ * k_cache, v_cache [B, Hkv, max_kv, head_dim]  in/out: row kv_lens[b] - 1 is
+ *              written with the rotated k_new / v_new (nothing is written for
+ *              a sequence whose row is outside [0, max_kv))
+ * kv_lens      [B] int32 device array: lengths INCLUDING the new token;
+ *              attention uses clamp(kv_lens[b], 0, max_kv) as attn_decode.
+ * position_ids [B] int32 device array, or NULL.
+ * out          [B, Hq, head_dim]
+ * workspace    at least rope_attn_decode_workspace_bytes(B, Hq, head_dim,
+ *              max_kv) bytes, 256-byte aligned, caller-owned, no initial
+ *              contents needed; concurrent calls must not share it.
+ * head_dim 64 or 128; Hq % Hkv == 0, Hq/Hkv <= 16; scale, theta,
+ * linear_factor > 0 and finite.
+ */
+rcgqa_status rope_attn_decode(const void* q, const void* k_new, const void* v_new,
+                              void* k_cache, void* v_cache,
+                              const int32_t* kv_lens, const int32_t* position_ids, void* out,
+                              int B, int Hq, int Hkv, int head_dim, int max_kv,
+                              float scale, float theta, float linear_factor,
+                              rcgqa_dtype dt, void* workspace, size_t workspace_bytes,
+                              rcgqa_stream stream);
+
 /* Static, human-readable name of a status code. */
 const char* rcgqa_status_string(rcgqa_status s);
 

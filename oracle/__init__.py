@@ -13,6 +13,8 @@ blocking, fusion or reordering beyond that definition:
                    mask (optionally a sliding window) and grouped-query head
                    sharing; single-token decode and chunked / variable-length
                    prefill against a cache.
+* ``fused``     -- rotation then attention, as one prefill or one decode step
+                   (with the cache append), composed from the two above.
 
 Pins (tests marked ``not gpu``) tie each function to something other than
 itself: closed forms, invariants, brute-force loops on tiny shapes, a library
@@ -21,6 +23,8 @@ and hand-derived fixtures under ``tests/golden``.
 """
 from .rope import inv_freq, angles, rotate, rope_apply
 from .attention import attention, attention_cache, attention_probs, decode, kv_append
+from .fused import rope_attention, rope_decode_step
 
 __all__ = ["inv_freq", "angles", "rotate", "rope_apply",
-           "attention", "attention_cache", "attention_probs", "decode", "kv_append"]
+           "attention", "attention_cache", "attention_probs", "decode", "kv_append",
+           "rope_attention", "rope_decode_step"]

@@ -48,6 +48,16 @@ def lib():
     L.attn_decode.restype = i32
     L.kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.kv_append.restype = i32
+    L.rope_attn_prefill_workspace_bytes.argtypes = [i32, i32, i32]
+    L.rope_attn_prefill_workspace_bytes.restype = sz
+    L.rope_attn_prefill.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, f32, f32, i32, vp, sz,
+                                    vp]
+    L.rope_attn_prefill.restype = i32
+    L.rope_attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
+    L.rope_attn_decode_workspace_bytes.restype = sz
+    L.rope_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, f32, i32, vp,
+                                   sz, vp]
+    L.rope_attn_decode.restype = i32
     L.rcgqa_status_string.argtypes = [i32]
     L.rcgqa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -197,3 +207,71 @@ def kv_append(k_cache, v_cache, k_new, v_new, slots):
                          _i32(slots, "slots", B), B, Hkv, D, max_kv, dt, _stream(k_cache))
     _check(st, "kv_append")
     return k_cache, v_cache
+
+
+def _workspace(need, like, workspace):
+    import torch
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=like.device)
+    return workspace, workspace.numel() * workspace.element_size()
+
+
+def rope_attn_prefill_workspace_bytes(B, S, head_dim):
+    return int(lib().rope_attn_prefill_workspace_bytes(B, S, head_dim))
+
+
+def rope_attn_prefill(q, k, v, position_ids=None, out=None, causal=True, scale=None, theta=10000.0,
+                      linear_factor=1.0, workspace=None):
+    """out [B,S,Hq,D] = attention(rope(q), rope(k), v); k is rotated in place,
+    q is left as it is (see rcgqa.h)."""
+    import torch
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B, S, Hq, D]")
+    pos = ctypes.c_void_p(0) if position_ids is None else _i32(position_ids, "position_ids", B * S)
+    workspace, wbytes = _workspace(rope_attn_prefill_workspace_bytes(B, S, D), q, workspace)
+    scale = D ** -0.5 if scale is None else scale
+    st = lib().rope_attn_prefill(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), _dev(v, "v", dt, 4),
+                                 _dev(out, "out", dt, 4), pos, B, S, Hq, Hkv, D, int(bool(causal)), float(scale),
+                                 float(theta), float(linear_factor), dt, _dev(workspace, "workspace"), wbytes,
+                                 _stream(q))
+    _check(st, "rope_attn_prefill")
+    return out
+
+
+def rope_attn_decode_workspace_bytes(B, Hq, head_dim, max_kv):
+    return int(lib().rope_attn_decode_workspace_bytes(B, Hq, head_dim, max_kv))
+
+
+def rope_attn_decode(q, k_new, v_new, k_cache, v_cache, kv_lens, position_ids=None, out=None, scale=None,
+                     theta=10000.0, linear_factor=1.0, workspace=None):
+    """One decode step: rotate q [B,Hq,D] and k_new [B,Hkv,D], append k_new/v_new at row
+    kv_lens[b]-1 of the caches [B,Hkv,max_kv,D], attend (see rcgqa.h)."""
+    import torch
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    _, Hkv, max_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, max_kv, D) or tuple(v_cache.shape) != (B, Hkv, max_kv, D):
+        raise ValueError("caches must be [B, Hkv, max_kv, D] matching q")
+    if tuple(k_new.shape) != (B, Hkv, D) or tuple(v_new.shape) != (B, Hkv, D):
+        raise ValueError("k_new/v_new must be [B, Hkv, D]")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B, Hq, D]")
+    pos = ctypes.c_void_p(0) if position_ids is None else _i32(position_ids, "position_ids", B)
+    workspace, wbytes = _workspace(rope_attn_decode_workspace_bytes(B, Hq, D, max_kv), q, workspace)
+    scale = D ** -0.5 if scale is None else scale
+    st = lib().rope_attn_decode(_dev(q, "q", dt, 3), _dev(k_new, "k_new", dt, 3), _dev(v_new, "v_new", dt, 3),
+                                _dev(k_cache, "k_cache", dt, 4), _dev(v_cache, "v_cache", dt, 4),
+                                _i32(kv_lens, "kv_lens", B), pos, _dev(out, "out", dt, 3), B, Hq, Hkv, D, max_kv,
+                                float(scale), float(theta), float(linear_factor), dt,
+                                _dev(workspace, "workspace"), wbytes, _stream(q))
+    _check(st, "rope_attn_decode")
+    return out

@@ -55,7 +55,7 @@ rcgqa_status rope_apply(void* q, void* k, const int32_t* position_ids, int B, in
   if (tokens < 0 || tokens > kI32Max || mul({tokens, Hq, head_dim}) < 0) return RCGQA_EINVAL;
   if (head_dim > 256) return RCGQA_EUNSUPPORTED;
   return hip_status(rcgqa::launch_rope(q, k, position_ids, B, S, Hq, Hkv, head_dim, (double)theta,
-                                       (double)linear_factor, dt == RCGQA_BF16, (hipStream_t)stream));
+                                       (double)linear_factor, dt == RCGQA_BF16, nullptr, (hipStream_t)stream));
 }
 
 rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq, int Hkv,
@@ -70,9 +70,10 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
   // K/V in [B, S, Hkv, D]: every sequence has S keys, queries aligned with them
   const rcgqa::KvSpec kv{(long long)S * Hkv * head_dim, head_dim, (long long)Hkv * head_dim, nullptr, S, 0};
   if (dt == RCGQA_BF16)
-    return hip_status(rcgqa::launch_prefill_bf16(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, kv, st));
+    return hip_status(
+        rcgqa::launch_prefill_bf16(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
   return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, B, S,
-                                              Hq, Hkv, head_dim, causal != 0, scale, kv, st));
+                                              Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
 }
 
 rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_lens,
@@ -93,9 +94,43 @@ rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* 
                          max_kv, window};
   if (dt == RCGQA_BF16)
     return hip_status(rcgqa::launch_prefill_bf16(q, k_cache, v_cache, out, B, Sq, Hq, Hkv, head_dim, causal != 0,
-                                                 scale, kv, st));
+                                                 scale, kv, nullptr, st));
   return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache,
-                                              (float*)out, B, Sq, Hq, Hkv, head_dim, causal != 0, scale, kv, st));
+                                              (float*)out, B, Sq, Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr,
+                                              st));
+}
+
+size_t rope_attn_prefill_workspace_bytes(int B, int S, int head_dim) {
+  const int64_t n = mul({B, S, head_dim, 4});
+  return n < 0 ? 0 : (size_t)n;
+}
+
+rcgqa_status rope_attn_prefill(const void* q, void* k, const void* v, void* out, const int32_t* position_ids,
+                               int B, int S, int Hq, int Hkv, int head_dim, int causal, float scale, float theta,
+                               float linear_factor, rcgqa_dtype dt, void* workspace, size_t workspace_bytes,
+                               rcgqa_stream stream) {
+  if (!q || !k || !v || !out || !workspace || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (out == q || out == k || out == v || q == k || k == v) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (!finite_pos(theta) || !finite_pos(linear_factor)) return RCGQA_EINVAL;
+  const int64_t tokens = mul({B, S});
+  if (tokens < 0 || tokens > kI32Max || mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0) return RCGQA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || (S + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  if (workspace_bytes < rope_attn_prefill_workspace_bytes(B, S, head_dim)) return RCGQA_EINVAL;
+  const hipStream_t st = (hipStream_t)stream;
+  float* table = (float*)workspace;
+  // keys rotated in place, each token's cos/sin kept for the queries
+  const hipError_t e = rcgqa::launch_rope(nullptr, k, position_ids, B, S, 0, Hkv, head_dim, (double)theta,
+                                          (double)linear_factor, dt == RCGQA_BF16, table, st);
+  if (e != hipSuccess) return RCGQA_EHIP;
+  const rcgqa::KvSpec kv{(long long)S * Hkv * head_dim, head_dim, (long long)Hkv * head_dim, nullptr, S, 0};
+  if (dt == RCGQA_BF16)
+    return hip_status(
+        rcgqa::launch_prefill_bf16(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, kv, table, st));
+  return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, B, S,
+                                              Hq, Hkv, head_dim, causal != 0, scale, kv, table, st));
 }
 
 size_t attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv) {
@@ -115,6 +150,40 @@ rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache
   if (workspace_bytes < rcgqa::decode_workspace_bytes(B, Hq, head_dim, max_kv)) return RCGQA_EINVAL;
   return hip_status(rcgqa::launch_decode(q, k_cache, v_cache, kv_lens, out, B, Hq, Hkv, head_dim, max_kv, scale,
                                          dt == RCGQA_BF16, workspace, (hipStream_t)stream));
+}
+
+size_t rope_attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv) {
+  if (!pos_int(B) || !pos_int(Hq) || !pos_int(head_dim) || !pos_int(max_kv)) return 0;
+  const int64_t qb = mul({B, Hq, head_dim, 4});
+  if (qb < 0) return 0;
+  return (size_t)((qb + 255) / 256 * 256) + rcgqa::decode_workspace_bytes(B, Hq, head_dim, max_kv);
+}
+
+rcgqa_status rope_attn_decode(const void* q, const void* k_new, const void* v_new, void* k_cache, void* v_cache,
+                              const int32_t* kv_lens, const int32_t* position_ids, void* out, int B, int Hq,
+                              int Hkv, int head_dim, int max_kv, float scale, float theta, float linear_factor,
+                              rcgqa_dtype dt, void* workspace, size_t workspace_bytes, rcgqa_stream stream) {
+  if (!q || !k_new || !v_new || !k_cache || !v_cache || !kv_lens || !out || !workspace || !good_dtype(dt))
+    return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (!finite_pos(theta) || !finite_pos(linear_factor)) return RCGQA_EINVAL;
+  if (B > 65535 || Hq > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0 || mul({B, Hq, head_dim, 4}) < 0)
+    return RCGQA_EINVAL;
+  if (reinterpret_cast<uintptr_t>(workspace) % 256) return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || Hq / Hkv > 16) return RCGQA_EUNSUPPORTED;
+  if (workspace_bytes < rope_attn_decode_workspace_bytes(B, Hq, head_dim, max_kv)) return RCGQA_EINVAL;
+  const hipStream_t st = (hipStream_t)stream;
+  // rotated queries first (256-byte aligned), the split-K partial states after them
+  const size_t qbytes = ((size_t)B * Hq * head_dim * 4 + 255) / 256 * 256;
+  void* q_rot = workspace;
+  void* ws = (char*)workspace + qbytes;
+  const hipError_t e =
+      rcgqa::launch_rope_append(q, q_rot, k_new, v_new, k_cache, v_cache, kv_lens, position_ids, B, Hq, Hkv, head_dim,
+                                max_kv, (double)theta, (double)linear_factor, dt == RCGQA_BF16, st);
+  if (e != hipSuccess) return RCGQA_EHIP;
+  return hip_status(rcgqa::launch_decode(q_rot, k_cache, v_cache, kv_lens, out, B, Hq, Hkv, head_dim, max_kv, scale,
+                                         dt == RCGQA_BF16, ws, st));
 }
 
 rcgqa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* slots,

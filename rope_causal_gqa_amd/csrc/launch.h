@@ -20,14 +20,27 @@ struct KvSpec {
   int window;
 };
 
+// q may be null with Hq == 0 (keys only).  table, when not null, receives each
+// token's fp32 cos/sin row ([B*S, D]: cos of pairs 0..D/2-1, then sin).
 hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
-                       double theta, double factor, bool bf16, hipStream_t st);
+                       double theta, double factor, bool bf16, float* table, hipStream_t st);
 
+// One decode step: rotate q into q_out and k_new at position pos[b] (kv_lens[b] - 1 when pos is null),
+// append the rotated key and v_new at row kv_lens[b] - 1 of the caches.
+hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, const int32_t* kv_lens, const int32_t* pos, int B, int Hq, int Hkv,
+                              int D, int max_kv, double theta, double factor, bool bf16, hipStream_t st);
+
+// q_rope, when not null, is the cos/sin table written by launch_rope for the
+// queries' tokens ([B*Sq, D]); the kernels then rotate each query row as they
+// load it, exactly as rope_apply would have.
 hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* out, int B, int Sq,
-                              int Hq, int Hkv, int D, bool causal, float scale, const KvSpec& kv, hipStream_t st);
+                              int Hq, int Hkv, int D, bool causal, float scale, const KvSpec& kv,
+                              const float* q_rope, hipStream_t st);
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int Sq,
-                               int Hq, int Hkv, int D, bool causal, float scale, const KvSpec& kv, hipStream_t st);
+                               int Hq, int Hkv, int D, bool causal, float scale, const KvSpec& kv,
+                               const float* q_rope, hipStream_t st);
 
 // Split-K decode: partial softmax states go to `ws`, then a merge pass writes out.
 size_t decode_workspace_bytes(int B, int Hq, int D, int max_kv);

@@ -75,7 +75,8 @@ template <int D, int NW, bool GEN, int KSPLIT>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
                                                              int Sq, int Hq, int Hkv, int causal, float c_log2,
-                                                             int nqt, int npairs, KvSpec kv) {
+                                                             int nqt, int npairs, KvSpec kv,
+                                                             const float* __restrict__ q_rope) {
   constexpr int NWG = NW / KSPLIT;  // waves per key group
   constexpr int BM = 32 * NWG;      // query rows per workgroup (32 per wave of a group)
   constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
@@ -124,6 +125,26 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)b * Sq + qrow) * qrs + (size_t)h * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) qf[ks] = src[2 * ks + hf];
+    if (q_rope) {
+      // Rotate the row by its token's cos/sin, with rope_apply's arithmetic.
+      // This lane holds elements 16 ks + 8 hf + e; the partner of pair i is
+      // i + D/2, i.e. the same e of k-step ks + KS/2 in the same lane.
+      const float* cs = q_rope + ((size_t)b * Sq + qrow) * D;
+#pragma unroll
+      for (int ks = 0; ks < KS / 2; ks++) {
+        const int i0 = 16 * ks + 8 * hf;
+        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + i0), c1 = *reinterpret_cast<const f32x4*>(cs + i0 + 4);
+        const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + D / 2 + i0);
+        const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + D / 2 + i0 + 4);
+#pragma unroll
+        for (int e = 0; e < 8; e++) {
+          const float co = e < 4 ? c0[e] : c1[e - 4], si = e < 4 ? s0[e] : s1[e - 4];
+          const float a = (float)qf[ks][e], bb = (float)qf[ks + KS / 2][e];
+          qf[ks][e] = (bf16)fmaf(a, co, -(bb * si));
+          qf[ks + KS / 2][e] = (bf16)fmaf(bb, co, a * si);
+        }
+      }
+    }
   } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) qf[ks] = bf16x8{};
@@ -360,29 +381,34 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
 
 template <int NW, bool GEN, int KSPLIT>
 static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
-                      int D, bool causal, float c_log2, int npairs, const KvSpec& kv, hipStream_t st) {
+                      int D, bool causal, float c_log2, int npairs, const KvSpec& kv, const float* q_rope,
+                      hipStream_t st) {
   constexpr int BM = 32 * NW / KSPLIT;
   const int nqt = (Sq + BM - 1) / BM;
   const dim3 grid((unsigned)((long long)B * Hq * npairs)), block(64 * NW);
   if (D == 64)
     hipLaunchKernelGGL((prefill_bf16_kernel<64, NW, GEN, KSPLIT>), grid, block, 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
+                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv,
+                       q_rope);
   else
     hipLaunchKernelGGL((prefill_bf16_kernel<128, NW, GEN, KSPLIT>), grid, block, 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv);
+                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv,
+                       q_rope);
 }
 
 template <int NW, int KSPLIT>
 static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
-                      int D, bool causal, float c_log2, int npairs, const KvSpec& kv, hipStream_t st) {
+                      int D, bool causal, float c_log2, int npairs, const KvSpec& kv, const float* q_rope,
+                      hipStream_t st) {
   if (kv.lens || kv.window > 0)
-    launch_nw<NW, true, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+    launch_nw<NW, true, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
   else
-    launch_nw<NW, false, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+    launch_nw<NW, false, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
 }
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
-                               int Hkv, int D, bool causal, float scale, const KvSpec& kv, hipStream_t st) {
+                               int Hkv, int D, bool causal, float scale, const KvSpec& kv, const float* q_rope,
+                               hipStream_t st) {
   const float c_log2 = (float)((double)scale * 1.4426950408889634);
   // Every K/V tile brought into LDS serves the workgroup's query rows, so 8
   // waves (256 rows) halve the tile traffic per flop against 4 waves (128
@@ -395,14 +421,14 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   const long long bh = (long long)B * Hq;
   const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
   if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512) {
-    launch_nw<8, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, kv, st);
+    launch_nw<8, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, kv, q_rope, st);
   } else {
     const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;
     const int npairs = pair4 ? (nqt4 + 1) / 2 : nqt4;
     if (bh * npairs >= 512)
-      launch_nw<4, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, st);
+      launch_nw<4, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
     else
-      launch_nw<8, 2>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, nqt4, kv, st);
+      launch_nw<8, 2>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, nqt4, kv, q_rope, st);
   }
   return hipGetLastError();
 }

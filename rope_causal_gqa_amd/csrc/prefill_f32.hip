@@ -21,7 +21,7 @@ template <int D>
 __global__ __launch_bounds__(64) void prefill_f32_kernel(const float* __restrict__ q, const float* __restrict__ k,
                                                          const float* __restrict__ v, float* __restrict__ out,
                                                          int Sq, int Hq, int Hkv, int causal, float scale,
-                                                         KvSpec kv) {
+                                                         KvSpec kv, const float* __restrict__ q_rope) {
   constexpr int BM = 64, BN = 32;
   __shared__ float4 sk[BN * D / 4], sv[BN * D / 4];
   const int bh = blockIdx.x, b = bh / Hq, h = bh - b * Hq;
@@ -42,6 +42,15 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const float* __restrict
   for (int d = 0; d < D; d++) {
     qr[d] = live ? qp[d] : 0.f;
     acc[d] = 0.f;
+  }
+  if (q_rope && live) {  // rotate the query row by its token's cos/sin (same arithmetic as rope_apply)
+    const float* cs = q_rope + ((size_t)b * Sq + i) * D;
+#pragma unroll
+    for (int d = 0; d < D / 2; d++) {
+      const float co = cs[d], si = cs[D / 2 + d], a = qr[d], bb = qr[D / 2 + d];
+      qr[d] = fmaf(a, co, -(bb * si));
+      qr[D / 2 + d] = fmaf(bb, co, a * si);
+    }
   }
   float m = -INFINITY, l = 0.f;
   // keys any row of this block can see: [key_lo, key_hi)
@@ -93,13 +102,15 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const float* __restrict
 }
 
 hipError_t launch_prefill_f32(const float* q, const float* k, const float* v, float* out, int B, int Sq, int Hq,
-                              int Hkv, int D, bool causal, float scale, const KvSpec& kv, hipStream_t st) {
+                              int Hkv, int D, bool causal, float scale, const KvSpec& kv, const float* q_rope,
+                              hipStream_t st) {
   const dim3 grid((unsigned)(B * Hq), (unsigned)((Sq + 63) / 64)), block(64);
   if (D == 64)
-    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, st, q, k, v, out, Sq, Hq, Hkv, (int)causal, scale, kv);
+    hipLaunchKernelGGL(prefill_f32_kernel<64>, grid, block, 0, st, q, k, v, out, Sq, Hq, Hkv, (int)causal, scale, kv,
+                       q_rope);
   else
     hipLaunchKernelGGL(prefill_f32_kernel<128>, grid, block, 0, st, q, k, v, out, Sq, Hq, Hkv, (int)causal, scale,
-                       kv);
+                       kv, q_rope);
   return hipGetLastError();
 }
 

@@ -11,6 +11,12 @@
 // that token then reuses them.  Each thread moves 16-byte vectors of the two
 // halves of a head vector, so loads and stores are fully coalesced.  The pass
 // is HBM-bound: it reads and writes every q/k element once.
+//
+// For the fused paths the same kernel can rotate K alone and write the
+// token's cos/sin row to a table (the prefill kernel then rotates Q as it
+// loads it, with the very same values and arithmetic), and a second kernel
+// rotates a decode step's q and new key and appends the key and value to the
+// cache in one launch.
 #include "common.h"
 #include "launch.h"
 
@@ -21,14 +27,8 @@ struct alignas(sizeof(T) * VE) Vec {
   T v[VE];
 };
 
-template <typename T, int VE>
-__global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restrict__ k,
-                                                   const int32_t* __restrict__ pos_ids, int S, int Hq,
-                                                   int Hkv, int D, double theta, double factor) {
-  extern __shared__ float cs[];  // cos[D/2] then sin[D/2]
-  const int tok = blockIdx.x;
+__device__ __forceinline__ void rope_angles(float* cs, int pos, int D, double theta, double factor) {
   const int half = D >> 1;
-  const int pos = pos_ids ? pos_ids[tok] : (tok % S);
   for (int i = threadIdx.x; i < half; i += blockDim.x) {
     const double inv = pow(theta, -2.0 * (double)i / (double)D);
     const double a = ((double)pos / factor) * inv;
@@ -37,46 +37,137 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
     cs[i] = (float)cn;
     cs[half + i] = (float)sn;
   }
+}
+
+// (x1, x2) -> (x1 c - x2 s, x2 c + x1 s) in fp32, rounded once to T: VE
+// elements of each half of one head vector, read at s1/s2 and written to d1/d2
+// (which may be the same addresses).
+template <typename T, int VE>
+__device__ __forceinline__ void rope_pair(const T* s1, const T* s2, T* d1, T* d2, const float* cs, int c, int half) {
+  const Vec<T, VE> x1 = *reinterpret_cast<const Vec<T, VE>*>(s1), x2 = *reinterpret_cast<const Vec<T, VE>*>(s2);
+  Vec<T, VE> y1, y2;
+#pragma unroll
+  for (int e = 0; e < VE; e++) {
+    const float co = cs[c * VE + e], si = cs[half + c * VE + e];
+    const float a = (float)x1.v[e], b = (float)x2.v[e];
+    y1.v[e] = (T)fmaf(a, co, -(b * si));
+    y2.v[e] = (T)fmaf(b, co, a * si);
+  }
+  *reinterpret_cast<Vec<T, VE>*>(d1) = y1;
+  *reinterpret_cast<Vec<T, VE>*>(d2) = y2;
+}
+
+// q may be null with Hq == 0 (keys only); table, when not null, receives the
+// token's cos/sin row: table[tok * D + i] = cos, table[tok * D + D/2 + i] = sin.
+template <typename T, int VE>
+__global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restrict__ k,
+                                                   const int32_t* __restrict__ pos_ids, int S, int Hq,
+                                                   int Hkv, int D, double theta, double factor,
+                                                   float* __restrict__ table) {
+  extern __shared__ float cs[];  // cos[D/2] then sin[D/2]
+  const int tok = blockIdx.x;
+  const int half = D >> 1;
+  const int pos = pos_ids ? pos_ids[tok] : (tok % S);
+  rope_angles(cs, pos, D, theta, factor);
   __syncthreads();
+  if (table)
+    for (int i = threadIdx.x; i < D; i += blockDim.x) table[(size_t)tok * D + i] = cs[i];
   const int cpr = half / VE;  // vectors per half head-vector
   const int units = (Hq + Hkv) * cpr;
   for (int u = threadIdx.x; u < units; u += blockDim.x) {
     const int head = u / cpr, c = u - head * cpr;
     T* base = head < Hq ? q + ((size_t)tok * Hq + head) * D : k + ((size_t)tok * Hkv + (head - Hq)) * D;
-    Vec<T, VE>* p1 = reinterpret_cast<Vec<T, VE>*>(base + c * VE);
-    Vec<T, VE>* p2 = reinterpret_cast<Vec<T, VE>*>(base + half + c * VE);
-    Vec<T, VE> x1 = *p1, x2 = *p2, y1, y2;
-#pragma unroll
-    for (int e = 0; e < VE; e++) {
-      const float co = cs[c * VE + e], si = cs[half + c * VE + e];
-      const float a = (float)x1.v[e], b = (float)x2.v[e];
-      y1.v[e] = (T)fmaf(a, co, -(b * si));
-      y2.v[e] = (T)fmaf(b, co, a * si);
-    }
-    *p1 = y1;
-    *p2 = y2;
+    rope_pair<T, VE>(base + c * VE, base + half + c * VE, base + c * VE, base + half + c * VE, cs, c, half);
+  }
+}
+
+// One decode step per sequence b (one workgroup each): rotate q[b] into
+// q_out[b] and k_new[b] at position pos_b, then write the rotated key and
+// v_new[b] into cache row slot_b = kv_lens[b] - 1 (nothing is written when
+// that row is outside [0, max_kv)).  pos_b = pos_ids[b], or slot_b when
+// pos_ids is null.  Same angles and arithmetic as rope_kernel.
+template <typename T, int VE>
+__global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ q, T* __restrict__ q_out,
+                                                          const T* __restrict__ k_new, const T* __restrict__ v_new,
+                                                          T* __restrict__ k_cache, T* __restrict__ v_cache,
+                                                          const int32_t* __restrict__ kv_lens,
+                                                          const int32_t* __restrict__ pos_ids, int Hq, int Hkv,
+                                                          int D, int max_kv, double theta, double factor) {
+  extern __shared__ float cs[];
+  const int b = blockIdx.x;
+  const int half = D >> 1;
+  const int slot = kv_lens[b] - 1;
+  const int pos = pos_ids ? pos_ids[b] : slot;
+  const bool write = slot >= 0 && slot < max_kv;
+  rope_angles(cs, pos, D, theta, factor);
+  __syncthreads();
+  const int cpr = half / VE;
+  for (int u = threadIdx.x; u < Hq * cpr; u += blockDim.x) {
+    const int head = u / cpr, c = u - head * cpr;
+    const size_t off = ((size_t)b * Hq + head) * D;
+    rope_pair<T, VE>(q + off + c * VE, q + off + half + c * VE, q_out + off + c * VE, q_out + off + half + c * VE, cs,
+                     c, half);
+  }
+  if (!write) return;
+  for (int u = threadIdx.x; u < Hkv * cpr; u += blockDim.x) {
+    const int head = u / cpr, c = u - head * cpr;
+    const size_t src = ((size_t)b * Hkv + head) * D;
+    const size_t dst = (((size_t)b * Hkv + head) * max_kv + slot) * D;
+    rope_pair<T, VE>(k_new + src + c * VE, k_new + src + half + c * VE, k_cache + dst + c * VE,
+                     k_cache + dst + half + c * VE, cs, c, half);
+    *reinterpret_cast<Vec<T, VE>*>(v_cache + dst + c * VE) = *reinterpret_cast<const Vec<T, VE>*>(v_new + src + c * VE);
+    *reinterpret_cast<Vec<T, VE>*>(v_cache + dst + half + c * VE) =
+        *reinterpret_cast<const Vec<T, VE>*>(v_new + src + half + c * VE);
   }
 }
 
 hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
-                       double theta, double factor, bool bf16_io, hipStream_t st) {
+                       double theta, double factor, bool bf16_io, float* table, hipStream_t st) {
   const dim3 grid((unsigned)((long)B * S)), block(256);
   const size_t lds = (size_t)D * sizeof(float);
   const int half = D / 2;
   if (bf16_io) {
     if (half % 8 == 0)
       hipLaunchKernelGGL((rope_kernel<bf16, 8>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq, Hkv, D,
-                         theta, factor);
+                         theta, factor, table);
     else
       hipLaunchKernelGGL((rope_kernel<bf16, 1>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq, Hkv, D,
-                         theta, factor);
+                         theta, factor, table);
   } else {
     if (half % 4 == 0)
       hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, lds, st, (float*)q, (float*)k, pos, S, Hq, Hkv,
-                         D, theta, factor);
+                         D, theta, factor, table);
     else
       hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, lds, st, (float*)q, (float*)k, pos, S, Hq, Hkv,
-                         D, theta, factor);
+                         D, theta, factor, table);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_append(const void* q, void* q_out, const void* k_new, const void* v_new, void* k_cache,
+                              void* v_cache, const int32_t* kv_lens, const int32_t* pos, int B, int Hq, int Hkv,
+                              int D, int max_kv, double theta, double factor, bool bf16_io, hipStream_t st) {
+  const dim3 grid((unsigned)B), block(256);
+  const size_t lds = (size_t)D * sizeof(float);
+  const int half = D / 2;
+  if (bf16_io) {
+    if (half % 8 == 0)
+      hipLaunchKernelGGL((rope_append_kernel<bf16, 8>), grid, block, lds, st, (const bf16*)q, (bf16*)q_out,
+                         (const bf16*)k_new, (const bf16*)v_new, (bf16*)k_cache, (bf16*)v_cache, kv_lens, pos, Hq,
+                         Hkv, D, max_kv, theta, factor);
+    else
+      hipLaunchKernelGGL((rope_append_kernel<bf16, 1>), grid, block, lds, st, (const bf16*)q, (bf16*)q_out,
+                         (const bf16*)k_new, (const bf16*)v_new, (bf16*)k_cache, (bf16*)v_cache, kv_lens, pos, Hq,
+                         Hkv, D, max_kv, theta, factor);
+  } else {
+    if (half % 4 == 0)
+      hipLaunchKernelGGL((rope_append_kernel<float, 4>), grid, block, lds, st, (const float*)q, (float*)q_out,
+                         (const float*)k_new, (const float*)v_new, (float*)k_cache, (float*)v_cache, kv_lens, pos,
+                         Hq, Hkv, D, max_kv, theta, factor);
+    else
+      hipLaunchKernelGGL((rope_append_kernel<float, 1>), grid, block, lds, st, (const float*)q, (float*)q_out,
+                         (const float*)k_new, (const float*)v_new, (float*)k_cache, (float*)v_cache, kv_lens, pos,
+                         Hq, Hkv, D, max_kv, theta, factor);
   }
   return hipGetLastError();
 }

@@ -146,3 +146,66 @@ def test_binding_requires_device_tensors():
         R.attn_prefill(q, q, q)
     with pytest.raises(ValueError):
         R.attn_prefill_cache(q, q, q, torch.zeros(1, dtype=torch.int32))
+
+
+def test_fused_workspace_bytes():
+    L = R.lib()
+    assert L.rope_attn_prefill_workspace_bytes(2, 4096, 128) == 2 * 4096 * 128 * 4
+    assert L.rope_attn_prefill_workspace_bytes(0, 4096, 128) == 0
+    d = L.rope_attn_decode_workspace_bytes(64, 64, 128, 8193)
+    assert d >= L.attn_decode_workspace_bytes(64, 64, 128, 8193) + 64 * 64 * 128 * 4
+    assert L.rope_attn_decode_workspace_bytes(1, 0, 128, 10) == 0
+
+
+@pytest.mark.parametrize("args", [
+    dict(ws=None), dict(wbytes=100), dict(ws_addr=4096 + 64), dict(q_is_k=True), dict(k_is_v=True),
+    dict(out_is_q=True), dict(Hq=6, Hkv=4), dict(theta=0.0), dict(factor=float("inf")), dict(causal=3),
+    dict(scale=0.0), dict(D=9),
+])
+def test_rope_attn_prefill_rejects(args):
+    a = dict(B=1, S=16, Hq=8, Hkv=2, D=64, causal=1, scale=0.125, theta=1e4, factor=1.0, ws_addr=4096 * 16,
+             wbytes=1 << 20)
+    a.update(args)
+    q, k, v, out = ctypes.c_void_p(4096), ctypes.c_void_p(8192), ctypes.c_void_p(12288), ctypes.c_void_p(16384)
+    if args.get("q_is_k"):
+        k = q
+    if args.get("k_is_v"):
+        v = k
+    if args.get("out_is_q"):
+        out = q
+    ws = None if "ws" in args else ctypes.c_void_p(a["ws_addr"])
+    st = R.lib().rope_attn_prefill(q, k, v, out, None, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["causal"],
+                                   a["scale"], a["theta"], a["factor"], 0, ws, a["wbytes"], None)
+    assert st == BD.EINVAL
+
+
+def test_rope_attn_prefill_unsupported_head_dim():
+    st = R.lib().rope_attn_prefill(FAKE, ctypes.c_void_p(8192), ctypes.c_void_p(12288), ctypes.c_void_p(16384),
+                                   None, 1, 16, 2, 2, 96, 1, 0.1, 1e4, 1.0, 0, ctypes.c_void_p(4096 * 16), 1 << 20,
+                                   None)
+    assert st == BD.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("args", [
+    dict(ws=None), dict(wbytes=0), dict(ws_addr=4096 + 8), dict(lens=None), dict(Hq=12, Hkv=8), dict(max_kv=0),
+    dict(theta=-1.0), dict(factor=0.0), dict(scale=float("nan")),
+])
+def test_rope_attn_decode_rejects(args):
+    a = dict(B=2, Hq=8, Hkv=2, D=128, max_kv=300, scale=0.1, theta=1e4, factor=2.0, ws_addr=4096 * 16,
+             wbytes=1 << 30, lens=FAKE)
+    a.update(args)
+    ws = None if "ws" in args else ctypes.c_void_p(a["ws_addr"])
+    st = R.lib().rope_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, a["lens"], None, ctypes.c_void_p(8192), a["B"],
+                                  a["Hq"], a["Hkv"], a["D"], a["max_kv"], a["scale"], a["theta"], a["factor"], 0, ws,
+                                  a["wbytes"], None)
+    assert st == BD.EINVAL
+
+
+def test_fused_binding_requires_device_tensors():
+    torch = pytest.importorskip("torch")
+    q = torch.zeros(1, 4, 2, 64)
+    with pytest.raises(ValueError):
+        R.rope_attn_prefill(q, q.clone(), q.clone())
+    with pytest.raises(ValueError):
+        R.rope_attn_decode(torch.zeros(1, 2, 64), torch.zeros(1, 1, 64), torch.zeros(1, 1, 64),
+                           torch.zeros(1, 1, 8, 64), torch.zeros(1, 1, 8, 64), torch.ones(1, dtype=torch.int32))

@@ -16,7 +16,8 @@ decode figure (GB/s of K/V bytes read, each row once per GQA group) rides in
 `decode`.  `roofline` is for the prefill kernel against the bf16 dense MFMA
 peak; `decode.roofline` against HBM.  `chunked_prefill` and `sliding_window`
 time the two prefill extensions (attn_prefill_cache) separately, after the
-timed steps.  `cpu_baseline` times the float64 oracle on a bounded sample on
+timed steps; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
+entry points against the separate calls on the same workloads.  `cpu_baseline` times the float64 oracle on a bounded sample on
 the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
@@ -135,6 +136,51 @@ def _next_rows(R, dev, stream):
     return out
 
 
+def _fused_rows(R, wp, wd, q, k, v, out, dq, dkn, dvn, kc, vc, ctx_d, lens_d, pos_d, dout, ws, stream):
+    """The fused RoPE paths against the separate calls, on the same two workloads
+    (outside the timed step):
+    * rope_attn_prefill (keys rotated in one pass that also writes the cos/sin
+      rows, queries rotated as the attention kernel loads them) vs rope_apply on
+      Q and K + attn_prefill;
+    * rope_attn_decode (q / new-key rotation and cache append in one kernel,
+      then the decode kernels) vs rope_apply + kv_append + attn_decode."""
+    import torch
+    dev = q.device
+    pws = torch.empty(R.rope_attn_prefill_workspace_bytes(wp.B, wp.S, wp.D), dtype=torch.uint8, device=dev)
+    dws = torch.empty(R.rope_attn_decode_workspace_bytes(wd.B, wd.Hq, wd.D, wd.max_kv), dtype=torch.uint8,
+                      device=dev)
+    fused_ms = _time_launches(lambda: R.rope_attn_prefill(q, k, v, None, out, causal=True, scale=wp.scale,
+                                                          theta=wp.theta, workspace=pws), stream)
+
+    def sep():
+        R.rope_apply(q, k, None, wp.theta, wp.factor)
+        R.attn_prefill(q, k, v, out, causal=True, scale=wp.scale)
+    sep_ms = _time_launches(sep, stream)
+    flops = wp.flops()
+    dq3 = dq.view(wd.B, wd.Hq, wd.D)
+    dkn3 = dkn.view(wd.B, wd.Hkv, wd.D)
+    dfused_ms = _time_launches(lambda: R.rope_attn_decode(dq3, dkn3, dvn, kc, vc, lens_d, None, dout, scale=wd.scale,
+                                                          theta=wd.theta, linear_factor=wd.factor, workspace=dws),
+                               stream)
+
+    def dsep():
+        R.rope_apply(dq, dkn, pos_d, wd.theta, wd.factor)
+        R.kv_append(kc, vc, dkn3, dvn, ctx_d)
+        R.attn_decode(dq3, kc, vc, lens_d, dout, scale=wd.scale, workspace=ws)
+    dsep_ms = _time_launches(dsep, stream)
+    return {
+        "fused_rope_prefill": {
+            "workload": "B=2 S=4096 Hq=Hkv=32 D=128 bf16 causal, RoPE theta 1e4 + attention",
+            "fused_ms": round(fused_ms, 4), "separate_ms": round(sep_ms, 4),
+            "speedup": round(sep_ms / fused_ms, 3),
+            "value": round(flops / (fused_ms * 1e-3) / 1e12, 2), "unit": "TFLOP/s (attention flops / whole call)"},
+        "fused_rope_decode": {
+            "workload": "B=64 Hq=64 Hkv=8 D=128 bf16, RoPE factor 2 at position = context, append + decode",
+            "fused_ms": round(dfused_ms, 4), "separate_ms": round(dsep_ms, 4),
+            "speedup": round(dsep_ms / dfused_ms, 3)},
+    }
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -239,6 +285,8 @@ def main():
     dec_gbps = dec_bytes / (dec_ms.mean() * 1e-3) / 1e9
     rope_bytes = 2.0 * wp.B * wp.S * (wp.Hq + wp.Hkv) * wp.D * 2
     extras = _next_rows(R, dev, stream)
+    fused = _fused_rows(R, wp, wd, q, k, v, out, dq, dkn, dvn, caches[0][0], caches[0][1], ctx_d, lens_d, pos_d,
+                        dout, ws, stream)
     res = {
         "metric": METRIC,
         "value": round(pre_tflops, 2),
@@ -270,6 +318,8 @@ def main():
         "hbm_copy_gbps": round(copy_gbps, 1),
         "chunked_prefill": extras["chunked_prefill"],
         "sliding_window": extras["sliding_window"],
+        "fused_rope_prefill": fused["fused_rope_prefill"],
+        "fused_rope_decode": fused["fused_rope_decode"],
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

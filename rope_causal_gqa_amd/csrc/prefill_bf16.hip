@@ -125,29 +125,25 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     const bf16x8* src = reinterpret_cast<const bf16x8*>(q + ((size_t)b * Sq + qrow) * qrs + (size_t)h * D);
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) qf[ks] = src[2 * ks + hf];
-    if (q_rope) {
-      // Rotate the row by its token's cos/sin, with rope_apply's arithmetic.
-      // This lane holds elements 16 ks + 8 hf + e; the partner of pair i is
-      // i + D/2, i.e. the same e of k-step ks + KS/2 in the same lane.
-      const float* cs = q_rope + ((size_t)b * Sq + qrow) * D;
-#pragma unroll
-      for (int ks = 0; ks < KS / 2; ks++) {
-        const int i0 = 16 * ks + 8 * hf;
-        const f32x4 c0 = *reinterpret_cast<const f32x4*>(cs + i0), c1 = *reinterpret_cast<const f32x4*>(cs + i0 + 4);
-        const f32x4 s0 = *reinterpret_cast<const f32x4*>(cs + D / 2 + i0);
-        const f32x4 s1 = *reinterpret_cast<const f32x4*>(cs + D / 2 + i0 + 4);
-#pragma unroll
-        for (int e = 0; e < 8; e++) {
-          const float co = e < 4 ? c0[e] : c1[e - 4], si = e < 4 ? s0[e] : s1[e - 4];
-          const float a = (float)qf[ks][e], bb = (float)qf[ks + KS / 2][e];
-          qf[ks][e] = (bf16)fmaf(a, co, -(bb * si));
-          qf[ks + KS / 2][e] = (bf16)fmaf(bb, co, a * si);
-        }
-      }
-    }
   } else {
 #pragma unroll
     for (int ks = 0; ks < KS; ks++) qf[ks] = bf16x8{};
+  }
+  // Cos/sin of the row's token when the queries still need their rotation
+  // (applied after the first tile's barrier, so these loads, the query loads
+  // and the first tile's direct loads are all in flight together).
+  f32x4 rc[KS / 2][2], rs[KS / 2][2];
+  const bool rot = q_rope && qrow < Sq;
+  if (rot) {
+    const float* cs = q_rope + ((size_t)b * Sq + qrow) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ks++) {
+      const int i0 = 16 * ks + 8 * hf;
+      rc[ks][0] = *reinterpret_cast<const f32x4*>(cs + i0);
+      rc[ks][1] = *reinterpret_cast<const f32x4*>(cs + i0 + 4);
+      rs[ks][0] = *reinterpret_cast<const f32x4*>(cs + D / 2 + i0);
+      rs[ks][1] = *reinterpret_cast<const f32x4*>(cs + D / 2 + i0 + 4);
+    }
   }
 
   // Tile loader: wave wr of a group fills tile rows [wr BN/NWG, (wr+1) BN/NWG) of K and V with
@@ -326,6 +322,20 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   if (tg_lo < tg_hi) issue(tg_lo, 0);
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
+  if (rot) {
+    // Rotate the row by its token's cos/sin, with rope_apply's arithmetic.
+    // This lane holds elements 16 ks + 8 hf + e; the partner of pair i is
+    // i + D/2, i.e. the same e of k-step ks + KS/2 in the same lane.
+#pragma unroll
+    for (int ks = 0; ks < KS / 2; ks++)
+#pragma unroll
+      for (int e = 0; e < 8; e++) {
+        const float co = rc[ks][e >> 2][e & 3], si = rs[ks][e >> 2][e & 3];
+        const float a = (float)qf[ks][e], bb = (float)qf[ks + KS / 2][e];
+        qf[ks][e] = (bf16)fmaf(a, co, -(bb * si));
+        qf[ks + KS / 2][e] = (bf16)fmaf(bb, co, a * si);
+      }
+  }
   for (int i = 0; i < steps; i += 2) {
     tile_step(tg_lo + i, std::integral_constant<int, 0>{});
     if (i + 1 < steps) tile_step(tg_lo + i + 1, std::integral_constant<int, 1>{});

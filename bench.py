@@ -20,7 +20,7 @@ timed steps; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
 entry points against the separate calls on the same workloads.  `cpu_baseline` times the float64 oracle on a bounded sample on
 the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline]
+    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
 """
 import argparse
 import hashlib
@@ -187,6 +187,9 @@ def main():
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extras", action="store_true",
+                    help="skip the prefill-extension and fused-RoPE timings after the steps "
+                         "(profiling runs that should see only the step's kernels)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported "
@@ -284,9 +287,11 @@ def main():
     pre_tflops = pre_flops / (pre_ms.mean() * 1e-3) / 1e12
     dec_gbps = dec_bytes / (dec_ms.mean() * 1e-3) / 1e9
     rope_bytes = 2.0 * wp.B * wp.S * (wp.Hq + wp.Hkv) * wp.D * 2
-    extras = _next_rows(R, dev, stream)
-    fused = _fused_rows(R, wp, wd, q, k, v, out, dq, dkn, dvn, caches[0][0], caches[0][1], ctx_d, lens_d, pos_d,
-                        dout, ws, stream)
+    extras, fused = {}, {}
+    if not args.no_extras:
+        extras = _next_rows(R, dev, stream)
+        fused = _fused_rows(R, wp, wd, q, k, v, out, dq, dkn, dvn, caches[0][0], caches[0][1], ctx_d, lens_d,
+                            pos_d, dout, ws, stream)
     res = {
         "metric": METRIC,
         "value": round(pre_tflops, 2),
@@ -316,10 +321,10 @@ def main():
         "rope": {"value": round(rope_bytes / (rope_ms.mean() * 1e-3) / 1e9, 1), "unit": "GB/s",
                  "launch_ms": round(float(rope_ms.mean()), 4)},
         "hbm_copy_gbps": round(copy_gbps, 1),
-        "chunked_prefill": extras["chunked_prefill"],
-        "sliding_window": extras["sliding_window"],
-        "fused_rope_prefill": fused["fused_rope_prefill"],
-        "fused_rope_decode": fused["fused_rope_decode"],
+        "chunked_prefill": extras.get("chunked_prefill"),
+        "sliding_window": extras.get("sliding_window"),
+        "fused_rope_prefill": fused.get("fused_rope_prefill"),
+        "fused_rope_decode": fused.get("fused_rope_decode"),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -96,7 +96,8 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
   extern __shared__ float cs[];
   const int b = blockIdx.x;
   const int half = D >> 1;
-  const int slot = kv_lens[b] - 1;
+  const int len = kv_lens[b];
+  const int slot = len > 0 ? len - 1 : -1;  // no overflow for any int32 length
   const int pos = pos_ids ? pos_ids[b] : slot;
   const bool write = slot >= 0 && slot < max_kv;
   rope_angles(cs, pos, D, theta, factor);

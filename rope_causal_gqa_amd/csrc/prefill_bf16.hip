@@ -8,7 +8,7 @@
 // Design (one workgroup = NW waves = 32 NW query rows of one (batch, head);
 // NW = 8 when the grid is large enough, else 4):
 //  * K/V tiles of 64 keys are double-buffered in LDS and filled with direct
-//    global->LDS loads (global_load_lds_dwordx4) one tile ahead of the math,
+//    global->LDS loads (buffer / global load ... lds) one tile ahead of the math,
 //    with a row-dependent XOR swizzle of 16-byte chunks so all three read
 //    patterns below are bank-conflict free.  One barrier per tile.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
@@ -33,6 +33,10 @@
 //    (keys through strides, per-sequence key counts, queries aligned to the
 //    end of their sequence) and the causal sliding window, whose tiles
 //    before the block's first window are never loaded either.
+//  * Given a per-token cos/sin table (written by the RoPE kernel while it
+//    rotates the keys), each lane rotates its query row in registers before
+//    the first tile ("LLaMA2大语言模型架构详解", section "Rotary Position
+//    Encoding"), so the queries never make a separate pass through memory.
 #include <type_traits>
 
 #include "common.h"

@@ -10,8 +10,10 @@
 // in LDS and read as wave-wide broadcasts.  Causal tiles past the block's last
 // row (and, with a sliding window, before its first window) are never loaded.
 // Keys come through strides and per-sequence counts, so the same kernel serves
-// chunked / variable-length prefill against a cache.  This path targets
-// accuracy (1e-5 against fp64), not throughput.
+// chunked / variable-length prefill against a cache.  Given a per-token
+// cos/sin table, each lane first rotates its query row (RoPE fused into the
+// load, same arithmetic as the RoPE kernel).  This path targets accuracy
+// (1e-5 against fp64), not throughput.
 #include "common.h"
 #include "launch.h"
 

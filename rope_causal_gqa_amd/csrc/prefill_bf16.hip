@@ -52,20 +52,37 @@ constexpr int PREF = 4;                  // K-operand LDS reads kept ahead of th
 constexpr int kSchedMfma = 0x008, kSchedDsRead = 0x100;
 }  // namespace
 
+// Direct global->LDS tile loads, 16 bytes per lane, landing at l + 16 * lane.
+//
+// They are written as inline asm rather than through the load-to-LDS
+// builtins on purpose.  The compiler's wait-count pass cannot tell the LDS
+// transpose reads (ds_read_b64_tr_b16, whose builtin carries no alias
+// information) apart from the tile being loaded, so with the builtins it puts
+// a wait for every load in flight in front of the first transpose read of
+// each tile: the P.V operands could then not be read before the next tile's
+// loads had landed.  Here completion is waited for explicitly, with a full
+// s_waitcnt before the per-tile barrier, and nothing reads a buffer that has
+// loads in flight before that barrier.  Each asm sets M0 (the LDS address of
+// the wave's 64 x 16 bytes) and leaves the one wait state the hardware needs
+// before the load reads it; nothing else in this kernel uses M0.
 __device__ __forceinline__ void lds_dma16(const void* g, bf16* l) {
-  __builtin_amdgcn_global_load_lds(g, (void __attribute__((address_space(3)))*)(l), 16, 0, 0);
+  const uint32_t m = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)l);
+  asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off" ::"v"(g), "s"(m));
 }
 
-// The same 16-byte-per-lane direct load through a buffer descriptor: the
-// tile's base lives in scalar registers and the per-lane byte offset `voff`
-// is fixed for the whole kernel, so issuing a tile takes no vector address
-// arithmetic.  The descriptor is raw (unstrided) with the largest range: every
-// offset used is inside the tensor by construction.  The last word is the
-// gfx9-family buffer format for untyped dword access.
+// The same load through a buffer descriptor: the tile's base lives in scalar
+// registers and the per-lane byte offset `voff` is fixed for the whole
+// kernel, so issuing a tile takes no vector address arithmetic.  The
+// descriptor is raw (unstrided) with the largest range: every offset used is
+// inside the tensor by construction.  The last word is the gfx9-family buffer
+// format for untyped dword access.
 __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16* l) {
-  const __amdgpu_buffer_rsrc_t rs =
-      __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xFFFFFFFF, 0x00020000);
-  __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (void __attribute__((address_space(3)))*)(l), 16, voff, 0, 0, 0);
+  typedef int i32x4 __attribute__((ext_vector_type(4)));
+  const uint64_t p = (uint64_t)base;
+  const i32x4 rs = {(int)(uint32_t)p, (int)((p >> 32) & 0xffff), (int)0xFFFFFFFF, 0x00020000};
+  const uint32_t m = (uint32_t)(uintptr_t)((__attribute__((address_space(3))) void*)l);
+  asm volatile("s_mov_b32 m0, %2\n\ts_nop 0\n\tbuffer_load_dwordx4 %0, %1, 0 offen lds" ::"v"(voff), "s"(rs),
+               "s"(m));
 }
 
 // GEN: keys through per-sequence counts (query rows aligned to the end of
@@ -261,6 +278,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         __builtin_amdgcn_sched_group_barrier(kSchedMfma, PREF, 0);
       }
 
+      // the first 16-key chunk of P.V operands is read now, so its latency
+      // hides under the softmax (the first P.V products then start as soon
+      // as the first eight weights exist)
+      bf16x8 vpre[DB];
+#pragma unroll
+      for (int db = 0; db < DB; db++)
+        vpre[db] = cat8(lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(sv) + voff[db][0])),
+                        lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(sv) + voff[db][1])));
+      __builtin_amdgcn_sched_barrier(0);
       // mask (diagonal / tail tiles only) and row max on raw scores
       if ((causal && kv0 + BN - 1 > wrow_lo + off) || kv0 + BN > nkeys || (W > 0 && kv0 <= wrow_hi + off - W)) {
 #pragma unroll
@@ -314,8 +340,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
 #pragma unroll
         for (int db = 0; db < DB; db++) {
           const char* vbase = reinterpret_cast<const char*>(sv) + kc * 16 * D * (int)sizeof(bf16);
-          const bf16x8 a = cat8(lds_read_tr16(reinterpret_cast<const bf16*>(vbase + voff[db][0])),
-                                lds_read_tr16(reinterpret_cast<const bf16*>(vbase + voff[db][1])));
+          const bf16x8 a = kc == 0 ? vpre[db]
+                                   : cat8(lds_read_tr16(reinterpret_cast<const bf16*>(vbase + voff[db][0])),
+                                          lds_read_tr16(reinterpret_cast<const bf16*>(vbase + voff[db][1])));
           o[db] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, pf[kc], o[db], 0, 0, 0);
         }
       }

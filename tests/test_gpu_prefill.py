@@ -193,3 +193,29 @@ def test_prefill_growing_scores(dtype, S, D):
     torch.cuda.synchronize()
     ref = oracle.attention(W.to_f64(q, dtype), W.to_f64(k, dtype), W.to_f64(v, dtype), True, scale)
     check(host64(out), ref, dtype, f"growing scores {dtype} S={S} D={D}")
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,causal", [(1, 16384, 4, 1, 128, True), (1, 12000, 8, 2, 64, False)])
+def test_prefill_long_sequence_sampled_rows(B, S, Hq, Hkv, D, causal):
+    """A long sequence (many query tiles, 32-bit tile offsets far into K/V):
+    sampled rows against the oracle, each as a single query over its visible
+    keys (the single-query form of the same attention, `attention_cache`)."""
+    import torch
+    announce(f"prefill long B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    seed = 900 + S
+    q = W.random_case(seed, (B, S, Hq, D), "bf16")
+    k = W.random_case(seed + 1, (B, S, Hkv, D), "bf16")
+    v = W.random_case(seed + 2, (B, S, Hkv, D), "bf16")
+    out = R.attn_prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), causal=causal, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    got = host64(out)
+    assert np.all(np.isfinite(got))
+    k64 = np.transpose(W.to_f64(k, "bf16"), (0, 2, 1, 3))     # [B, Hkv, S, D] cache layout
+    v64 = np.transpose(W.to_f64(v, "bf16"), (0, 2, 1, 3))
+    q64 = W.to_f64(q, "bf16")
+    rows = [0, 1, 63, 64, 4095, 8191, S // 2 + 17, S - 65, S - 2, S - 1]
+    for i in rows:
+        L = i + 1 if causal else S
+        ref = oracle.attention_cache(q64[:, i:i + 1], k64, v64, np.full(B, L), causal, D ** -0.5)
+        # with causal, the single query at position L-1 is row i; without, it sees all S keys
+        check(got[:, i:i + 1], ref, "bf16", f"long row {i}")

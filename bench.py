@@ -16,7 +16,9 @@ decode figure (GB/s of K/V bytes read, each row once per GQA group) rides in
 `decode`.  `roofline` is for the prefill kernel against the bf16 dense MFMA
 peak; `decode.roofline` against HBM.  `chunked_prefill` and `sliding_window`
 time the two prefill extensions (attn_prefill_cache) separately, after the
-timed steps; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
+timed steps; `gqa_prefill` times attn_prefill on the LLaMA-70B-shaped GQA
+prefill (B=1 S=4096 Hq=64 Hkv=8 D=128) and on its 8-query-head / 1-KV-head
+share; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
 entry points against the separate calls on the same workloads.  `cpu_baseline` times the float64 oracle on a bounded sample on
 the host cores.
 
@@ -133,6 +135,22 @@ def _next_rows(R, dev, stream):
                      "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
         del q, kc, vc, o
+    from rope_causal_gqa_amd import workloads as W
+    gqa = {}
+    for name in ("c4a", "c4b"):
+        w = W.WORKLOADS[name]
+        q = torch.randn((w.B, w.S, w.Hq, w.D), generator=g, device=dev).to(torch.bfloat16)
+        k = torch.randn((w.B, w.S, w.Hkv, w.D), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((w.B, w.S, w.Hkv, w.D), generator=g, device=dev).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        ms = _time_launches(lambda: R.attn_prefill(q, k, v, o, causal=True, scale=w.scale), stream)
+        tf = w.flops() / (ms * 1e-3) / 1e12
+        gqa[name] = {"workload": f"{w.name}: B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D} bf16 causal",
+                     "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 4),
+                     "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                  "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+        del q, k, v, o
+    out["gqa_prefill"] = [gqa["c4a"], gqa["c4b"]]
     return out
 
 
@@ -311,7 +329,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic("prefill_c3", PREFILL_KERNEL_SRC),
-                     "kernel": "prefill_bf16_kernel<128, 8>", "launch_ms": round(float(pre_ms.mean()), 4)},
+                     "kernel": "prefill_bf16_kernel<128, 8, false, 1, 64>", "launch_ms": round(float(pre_ms.mean()), 4)},
         "decode": {"metric": "decode KV-cache GB/s", "value": round(dec_gbps, 1), "unit": "GB/s",
                    "launch_ms": round(float(dec_ms.mean()), 4),
                    "algorithmic_bytes": dec_bytes,
@@ -323,6 +341,7 @@ def main():
         "hbm_copy_gbps": round(copy_gbps, 1),
         "chunked_prefill": extras.get("chunked_prefill"),
         "sliding_window": extras.get("sliding_window"),
+        "gqa_prefill": extras.get("gqa_prefill"),
         "fused_rope_prefill": fused.get("fused_rope_prefill"),
         "fused_rope_decode": fused.get("fused_rope_decode"),
         "cpu_baseline": None,

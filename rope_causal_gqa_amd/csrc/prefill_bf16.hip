@@ -37,6 +37,9 @@
 //    rotates the keys), each lane rotates its query row in registers before
 //    the first tile ("LLaMA2大语言模型架构详解", section "Rotary Position
 //    Encoding"), so the queries never make a separate pass through memory.
+#include <algorithm>
+#include <functional>
+#include <vector>
 #include <type_traits>
 
 #include "common.h"
@@ -45,7 +48,6 @@
 namespace rcgqa {
 
 namespace {
-constexpr int BN = 64;                   // keys per K/V tile
 constexpr float kRescaleLog2 = 8.f;      // lazy rescale threshold (log2 units)
 constexpr int PREF = 4;                  // K-operand LDS reads kept ahead of the MFMAs
 // instruction classes of __builtin_amdgcn_sched_group_barrier
@@ -88,16 +90,20 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
 // GEN: keys through per-sequence counts (query rows aligned to the end of
 // their sequence) and an optional sliding window; without it every sequence
 // has Sq keys, queries and keys aligned, and the bounds fold to constants.
-// KSPLIT = 2: the NW waves form two groups that take the same 32*NW/2 query
-// rows over the two halves of the key range, each with its own LDS tiles, and
-// merge their softmax states through LDS at the end (more waves in flight for
-// grids too small to fill the GPU, with no memory outside the workgroup).
-template <int D, int NW, bool GEN, int KSPLIT>
+// KSPLIT > 1: the NW waves form KSPLIT groups that take the same 32*NW/KSPLIT
+// query rows over consecutive parts of the key range, each with its own LDS
+// tiles, and merge their softmax states through LDS at the end (more waves in
+// flight for grids too small to fill the GPU, with no memory outside the
+// workgroup).  BNT keys per K/V tile: 64, or 32 so that four groups' double
+// buffers fit in LDS.
+template <int D, int NW, bool GEN, int KSPLIT, int BNT>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
                                                              int Sq, int Hq, int Hkv, int causal, float c_log2,
                                                              int nqt, int npairs, KvSpec kv,
                                                              const float* __restrict__ q_rope) {
+  constexpr int BN = BNT;           // keys per K/V tile
+  constexpr int NKB = BN / 32;      // 32-key blocks per tile
   constexpr int NWG = NW / KSPLIT;  // waves per key group
   constexpr int BM = 32 * NWG;      // query rows per workgroup (32 per wave of a group)
   constexpr int KS = D / 16;  // k-steps of the Q K^T contraction
@@ -136,7 +142,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   // this sequence's keys; query i sits at absolute position i + off
   const int nkeys = GEN ? min(max(kv.lens[b], 0), kv.max_kv) : Sq;
   const int off = GEN ? nkeys - Sq : 0, W = GEN ? kv.window : 0;
-  const int qt_first = npairs < nqt ? nqt - 1 - slot : slot;
+  // heavy (late) causal query tiles first: with more workgroups than fit at
+  // once, the light ones then fill in behind them
+  const int qt_first = (npairs < nqt || causal) ? nqt - 1 - slot : slot;
   const int npass = (npairs < nqt && slot != nqt - 1 - slot) ? 2 : 1;
   auto run_qtile = [&](const int q0) __attribute__((always_inline)) {
 
@@ -219,7 +227,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int key_hi = causal ? min(nkeys, q0 + BM + off) : nkeys;
   const int key_lo = (causal && W > 0) ? max(0, q0 + off - W + 1) : 0;
   const int t_lo = key_lo / BN, t_hi = key_hi > 0 ? (key_hi + BN - 1) / BN : 0;
-  // this group's tiles [tg_lo, tg_hi); both groups run `steps` barrier steps
+  // this group's tiles [tg_lo, tg_hi) (possibly empty); all groups run `steps` barrier steps
   const int ntl = max(t_hi - t_lo, 0), steps = (ntl + KSPLIT - 1) / KSPLIT;
   const int tg_lo = t_lo + grp * steps, tg_hi = min(tg_lo + steps, t_lo + ntl);
   const int wrow_lo = q0 + wr * 32, wrow_hi = wrow_lo + 31;
@@ -257,12 +265,14 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       const bf16* sk = ldsg + buf * 2 * TILE;
       const bf16* sv = sk + TILE;
 
-      // S^T = K Q^T: two 32-key blocks, chains interleaved
-      f32x16 s[2] = {f32x16{}, f32x16{}};
+      // S^T = K Q^T: NKB 32-key blocks, chains interleaved
+      f32x16 s[NKB];
+#pragma unroll
+      for (int kb2 = 0; kb2 < NKB; kb2++) s[kb2] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; kb2++) {
+        for (int kb2 = 0; kb2 < NKB; kb2++) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(sk) + koff[ks] +
                                                             kb2 * 32 * D * (int)sizeof(bf16));
           s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
@@ -271,7 +281,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       if (PREF > 0) {
         __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PREF, 0);
 #pragma unroll
-        for (int i = 0; i < 2 * KS - PREF; i++) {
+        for (int i = 0; i < NKB * KS - PREF; i++) {
           __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
           __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
         }
@@ -290,7 +300,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       // mask (diagonal / tail tiles only) and row max on raw scores
       if ((causal && kv0 + BN - 1 > wrow_lo + off) || kv0 + BN > nkeys || (W > 0 && kv0 <= wrow_hi + off - W)) {
 #pragma unroll
-        for (int kb2 = 0; kb2 < 2; kb2++)
+        for (int kb2 = 0; kb2 < NKB; kb2++)
 #pragma unroll
           for (int i = 0; i < 16; i++) {
             const int key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
@@ -301,7 +311,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
 #pragma unroll
       for (int i = 1; i < 16; i++) mx = fmaxf(mx, s[0][i]);
 #pragma unroll
-      for (int i = 0; i < 16; i++) mx = fmaxf(mx, s[1][i]);
+      for (int kb2 = 1; kb2 < NKB; kb2++)
+#pragma unroll
+        for (int i = 0; i < 16; i++) mx = fmaxf(mx, s[kb2][i]);
       mx = half_swap_max(mx);
 
       // lazy rescale: move the reference max only when some row grew by more
@@ -316,9 +328,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         m_lim = m_new + rescale_margin;
         nmc = -m_new * c_log2;
       }
-      bf16x8 pf[4];
+      bf16x8 pf[2 * NKB];
 #pragma unroll
-      for (int kb2 = 0; kb2 < 2; kb2++) {
+      for (int kb2 = 0; kb2 < NKB; kb2++) {
 #pragma unroll
         for (int i = 0; i < 16; i++) pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)fast_exp2(fmaf(s[kb2][i], c_log2, nmc));
       }
@@ -326,7 +338,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       // two chains, one of them continuing the running sum)
       float sa = l_run, sb = 0.f;
 #pragma unroll
-      for (int j = 0; j < 4; j++)
+      for (int j = 0; j < 2 * NKB; j++)
 #pragma unroll
         for (int e = 0; e < 4; e += 2) {
           sa = bf16_pair_sum(pf[j][2 * e], pf[j][2 * e + 1], sa);
@@ -334,9 +346,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         }
       l_run = sa + sb;
 
-      // O^T += V^T P^T over four 16-key chunks
+      // O^T += V^T P^T over the tile's 16-key chunks
 #pragma unroll
-      for (int kc = 0; kc < 4; kc++) {
+      for (int kc = 0; kc < 2 * NKB; kc++) {
 #pragma unroll
         for (int db = 0; db < DB; db++) {
           const char* vbase = reinterpret_cast<const char*>(sv) + kc * 16 * D * (int)sizeof(bf16);
@@ -371,13 +383,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     tile_step(tg_lo + i, std::integral_constant<int, 0>{});
     if (i + 1 < steps) tile_step(tg_lo + i + 1, std::integral_constant<int, 1>{});
   }
-  if constexpr (KSPLIT == 2) {
-    // The second key group hands its state to its partner wave (same rows,
-    // same lane layout) through LDS; every tile is consumed and no load is in
-    // flight since the last step's barrier.
+  if constexpr (KSPLIT > 1) {
+    static_assert((KSPLIT - 1) * NWG * (DB * 16 + 2) * 64 * sizeof(float) <= sizeof(lds), "hand-over area");
+    // Key groups 1.. hand their states to their partner waves of group 0
+    // (same rows, same lane layout) through LDS, merged in group order; every
+    // tile is consumed and no load is in flight since the last step's barrier.
     constexpr int NV = DB * 16 + 2;
-    float* xfer = reinterpret_cast<float*>(lds) + (size_t)wr * NV * 64 + lane;
-    if (grp == 1) {
+    auto xslot = [&](int g) __attribute__((always_inline)) {
+      return reinterpret_cast<float*>(lds) + ((size_t)(g - 1) * NWG + wr) * NV * 64 + lane;
+    };
+    if (grp > 0) {
+      float* xfer = xslot(grp);
 #pragma unroll
       for (int db = 0; db < DB; db++)
 #pragma unroll
@@ -387,14 +403,19 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     }
     __syncthreads();
     if (grp == 0) {
-      const float m1 = xfer[(DB * 16) * 64], l1 = xfer[(DB * 16 + 1) * 64];
-      const float m = fmaxf(m_run, m1);
-      const float a0 = fast_exp2((m_run - m) * c_log2), a1 = fast_exp2((m1 - m) * c_log2);
-      l_run = l_run * a0 + l1 * a1;
 #pragma unroll
-      for (int db = 0; db < DB; db++)
+      for (int g = 1; g < KSPLIT; g++) {
+        const float* xfer = xslot(g);
+        const float m1 = xfer[(DB * 16) * 64], l1 = xfer[(DB * 16 + 1) * 64];
+        const float m = fmaxf(m_run, m1);
+        const float a0 = fast_exp2((m_run - m) * c_log2), a1 = fast_exp2((m1 - m) * c_log2);
+        l_run = l_run * a0 + l1 * a1;
 #pragma unroll
-        for (int i = 0; i < 16; i++) o[db][i] = o[db][i] * a0 + xfer[(db * 16 + i) * 64] * a1;
+        for (int db = 0; db < DB; db++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) o[db][i] = o[db][i] * a0 + xfer[(db * 16 + i) * 64] * a1;
+        m_run = m;
+      }
     }
     __syncthreads();  // the hand-over area is free again before any later tile load
   }
@@ -420,7 +441,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   if (npass == 2) run_qtile(slot * BM);
 }
 
-template <int NW, bool GEN, int KSPLIT>
+template <int NW, bool GEN, int KSPLIT, int BNT>
 static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
                       int D, bool causal, float c_log2, int npairs, const KvSpec& kv, const float* q_rope,
                       hipStream_t st) {
@@ -428,24 +449,102 @@ static void launch_nw(const void* q, const void* k, const void* v, void* out, in
   const int nqt = (Sq + BM - 1) / BM;
   const dim3 grid((unsigned)((long long)B * Hq * npairs)), block(64 * NW);
   if (D == 64)
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW, GEN, KSPLIT>), grid, block, 0, st, (const bf16*)q,
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW, GEN, KSPLIT, BNT>), grid, block, 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv,
                        q_rope);
   else
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW, GEN, KSPLIT>), grid, block, 0, st, (const bf16*)q,
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW, GEN, KSPLIT, BNT>), grid, block, 0, st, (const bf16*)q,
                        (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv,
                        q_rope);
 }
 
-template <int NW, int KSPLIT>
+template <int NW, int KSPLIT, int BNT = 64>
 static void launch_nw(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq, int Hkv,
                       int D, bool causal, float c_log2, int npairs, const KvSpec& kv, const float* q_rope,
                       hipStream_t st) {
   if (kv.lens || kv.window > 0)
-    launch_nw<NW, true, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
+    launch_nw<NW, true, KSPLIT, BNT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
   else
-    launch_nw<NW, false, KSPLIT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
+    launch_nw<NW, false, KSPLIT, BNT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
 }
+
+namespace {
+constexpr int kCUs = 256;  // compute units of a gfx950 MI355X
+
+// sum over query rows i in [a, b) of min(max(i + c, 0), cap): the keys those rows see
+double rows_keys(long long a, long long b, long long c, long long cap) {
+  const long long z = std::min(std::max(a, 1 - c), b);    // first row that sees a key
+  const long long u = std::min(std::max(z, cap - c), b);  // first row that sees cap keys
+  return 0.5 * (double)(u - z) * (double)(z + c + u - 1 + c) + (double)(b - u) * (double)cap;
+}
+
+// Finish time of the busiest CU for a grid of
+// bh * w.size() workgroups (work item i = head i / w.size(), slot i % w.size(),
+// taking time w[slot]) that run one per CU: each XCD takes its share of the
+// work list (see the kernel's work mapping) in order and hands every item to
+// whichever of its CUs frees first.
+double busiest_cu(const std::vector<double>& w, long long bh) {
+  const long long n = bh * (long long)w.size();
+  const int per_xcd = kCUs / 8;
+  double worst = 0;
+  std::vector<double> load(per_xcd);
+  for (int x = 0; x < 8; x++) {
+    std::fill(load.begin(), load.end(), 0.0);  // a min-heap of this XCD's CU loads
+    auto take = [&](long long item) {
+      std::pop_heap(load.begin(), load.end(), std::greater<double>());
+      load.back() += w[item % (long long)w.size()];
+      std::push_heap(load.begin(), load.end(), std::greater<double>());
+    };
+    if (n % 8 == 0)
+      for (long long i = x * (n / 8); i < (x + 1) * (n / 8); i++) take(i);
+    else
+      for (long long i = x; i < n; i += 8) take(i);
+    worst = std::max(worst, *std::max_element(load.begin(), load.end()));
+  }
+  return worst;
+}
+
+// For query counts too small for 512 workgroups of 4 waves there are two
+// grids: 128-row tiles in two key groups (A) and 64-row tiles in four key
+// groups over 32-key K/V tiles (B, causal tiles paired when that keeps 256
+// workgroups).  B cuts the work finer; A moves half the K/V tile traffic per
+// flop, runs 64-key steps and sets up one tile per workgroup.  Each grid's
+// workgroup time is modelled as a set-up cost per query tile plus its
+// (query row, key) pairs over a rate, both fitted to MI355X timings of the
+// two kernels (A: 3.1 us + pairs / 7.3e3 per us; B: 7.5 us per tile + pairs
+// / 6.1e3 per us), and B is taken when it is estimated to finish first.
+// Rows see keys by the causal and window rules, caches taken as full.
+bool four_groups_model(long long bh, int Sq, bool causal, const KvSpec& kv, int nqt2, int npairs2, int nqt4) {
+  constexpr double kSetupA = 3.1, kRateA = 7.3e3, kSetupB = 7.5, kRateB = 6.1e3;
+  const long long nk = kv.lens ? kv.max_kv : Sq;
+  const long long c = causal ? nk - Sq + 1 : nk, cap = kv.window > 0 ? std::min<long long>(kv.window, nk) : nk;
+  // heavy (late) tiles first, as the kernel orders them
+  std::vector<double> wa(nqt4), wb(npairs2);
+  for (int t = 0; t < nqt4; t++) {
+    const int qt = causal ? nqt4 - 1 - t : t;
+    wa[t] = kSetupA + rows_keys(128LL * qt, std::min(128LL * qt + 128, (long long)Sq), c, cap) / kRateA;
+  }
+  auto w2 = [&](int qt) { return kSetupB + rows_keys(64LL * qt, std::min(64LL * qt + 64, (long long)Sq), c, cap) / kRateB; };
+  for (int p = 0; p < npairs2; p++) {
+    const int qt = causal ? nqt2 - 1 - p : p;
+    wb[p] = w2(qt) + (npairs2 < nqt2 && p != qt ? w2(p) : 0.0);
+  }
+  return busiest_cu(wb, bh) < busiest_cu(wa, bh);
+}
+
+// The choice for the last shape seen on this thread is kept: serving loops
+// repeat shapes, and the estimate walks every workgroup of both grids.
+bool four_groups_first(long long bh, int Sq, bool causal, const KvSpec& kv, int nqt2, int npairs2, int nqt4) {
+  const long long key[5] = {bh, Sq, causal, kv.lens ? kv.max_kv : -1, kv.window};
+  thread_local long long last[5] = {-1, -1, -1, -1, -1};
+  thread_local bool last_choice = false;
+  if (!std::equal(key, key + 5, last)) {
+    last_choice = four_groups_model(bh, Sq, causal, kv, nqt2, npairs2, nqt4);
+    std::copy(key, key + 5, last);
+  }
+  return last_choice;
+}
+}  // namespace
 
 hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
                                int Hkv, int D, bool causal, float scale, const KvSpec& kv, const float* q_rope,
@@ -457,8 +556,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   // Causal grids pair heavy and light query tiles so all workgroups do equal
   // work.  In order of preference: 8 waves when that paired grid still has
   // 512 workgroups or more; 4 waves when their grid (paired if that keeps 512
-  // workgroups) has 512 or more; otherwise 8 waves in two key groups over
-  // 128-row tiles, so a grid of fewer workgroups still runs 8 waves per CU.
+  // workgroups) has 512 or more; otherwise one 8-wave workgroup per CU in
+  // several key groups, 128-row tiles in two groups or 64-row tiles in four,
+  // whichever is estimated to finish first.
   const long long bh = (long long)B * Hq;
   const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
   if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512) {
@@ -466,10 +566,16 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   } else {
     const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;
     const int npairs = pair4 ? (nqt4 + 1) / 2 : nqt4;
-    if (bh * npairs >= 512)
+    const int nqt2 = (Sq + 63) / 64;
+    if (bh * npairs >= 512) {
       launch_nw<4, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
-    else
-      launch_nw<8, 2>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, nqt4, kv, q_rope, st);
+    } else {
+      const int npairs2 = causal && nqt2 > 1 && bh * ((nqt2 + 1) / 2) >= 256 ? (nqt2 + 1) / 2 : nqt2;
+      if (four_groups_first(bh, Sq, causal, kv, nqt2, npairs2, nqt4))
+        launch_nw<8, 4, 32>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs2, kv, q_rope, st);
+      else
+        launch_nw<8, 2>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, nqt4, kv, q_rope, st);
+    }
   }
   return hipGetLastError();
 }

@@ -134,10 +134,43 @@ def test_prefill_eight_wave_grid(B, S, Hq, Hkv, D, heads):
         check(got[b, :, h], ref[b, :, h], "bf16", f"8-wave B={B} S={S} b={b} h={h}")
 
 
-@pytest.mark.parametrize("name", ["c2b", "c3"])
+# Grids too small for 512 workgroups of 4 waves run one 8-wave workgroup per
+# CU, in two key groups over 128-row tiles or four over 64-row tiles,
+# whichever the launcher estimates to finish first.  These shapes take the
+# four-group kernel (paired causal tiles, unpaired causal tiles with D=64,
+# non-causal; ragged tails) and, last, the two-group one.
+FOUR = [
+    # B, S, Hq, Hkv, D, causal
+    (1, 4000, 8, 2, 128, True),
+    (1, 2100, 8, 1, 64, True),
+    (1, 2000, 8, 2, 128, False),
+    (1, 2100, 16, 2, 128, True),
+]
+
+
+@pytest.mark.parametrize("B,S,Hq,Hkv,D,causal", FOUR)
+def test_prefill_key_groups(B, S, Hq, Hkv, D, causal):
+    import torch
+    announce(f"prefill key groups B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} causal={causal}")
+    seed = 9 + B * 7 + S * 13 + Hq * 17 + D
+    q = W.random_case(seed, (B, S, Hq, D), "bf16")
+    k = W.random_case(seed + 1, (B, S, Hkv, D), "bf16")
+    v = W.random_case(seed + 2, (B, S, Hkv, D), "bf16")
+    scale = 1.0 / math.sqrt(D)
+    n = B * S * Hq * D
+    buf = torch.full((n + 2048,), 7.0, dtype=torch.bfloat16, device="cuda")
+    out = buf[1024:1024 + n].view(B, S, Hq, D)
+    R.attn_prefill(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), out, causal=causal, scale=scale)
+    torch.cuda.synchronize()
+    assert torch.all(buf[:1024] == 7.0) and torch.all(buf[1024 + n:] == 7.0), "write outside out"
+    ref = oracle.attention(W.to_f64(q, "bf16"), W.to_f64(k, "bf16"), W.to_f64(v, "bf16"), causal, scale)
+    check(host64(out), ref, "bf16", f"key groups B={B} S={S} Hq={Hq} D={D} c={causal}")
+
+
+@pytest.mark.parametrize("name", ["c2b", "c3", "c4b"])
 def test_prefill_deterministic(name):
     """Repeated launches give bitwise equal results (c3 takes the 8-wave
-    kernel, c2b the 4-wave one)."""
+    kernel, c2b the 4-wave one, c4b the one with four key groups)."""
     import torch
     w = W.WORKLOADS[name]
     g = torch.Generator(device="cuda")

@@ -46,6 +46,10 @@ CASES = [
     (2, 200, 4, 2, 128, 400, [260, 400], 1, 5000, "bf16"),     # window longer than the cache
     (2, 1, 16, 2, 128, 700, [513, 700], 1, 0, "bf16"),         # one token: a decode step
     (1, 513, 2, 1, 128, 1500, [1500], 1, 300, "bf16"),         # window with tile-unaligned edges
+    (1, 2100, 8, 1, 128, 3000, [2900], 1, 0, "bf16"),          # four key groups over 64-row tiles
+    (1, 3000, 4, 2, 64, 3100, [3100], 1, 1500, "bf16"),        # four key groups, window
+    (2, 2000, 4, 2, 128, 1900, [1900, 1000], 0, 0, "bf16"),    # four key groups, non-causal
+    (1, 2100, 16, 2, 64, 2600, [2500], 1, 700, "bf16"),        # two key groups, window
     (2, 70, 4, 2, 64, 200, [150, 70], 1, 0, "fp32"),
     (2, 33, 8, 2, 128, 120, [20, 120], 1, 17, "fp32"),
     (1, 50, 2, 1, 64, 90, [90], 0, 0, "fp32"),

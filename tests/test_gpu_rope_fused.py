@@ -35,6 +35,7 @@ PRE_CASES = [
     (2, 70, 4, 2, 64, True, "fp32", "offsets", 1e4, 2.0),
     (1, 1024, 64, 8, 128, True, "bf16", "arange", 1e4, 1.0),   # GQA, 4-wave grid
     (2, 2048, 32, 32, 128, True, "bf16", "arange", 1e4, 1.0),  # 8-wave grid
+    (1, 2100, 8, 1, 128, True, "bf16", "offsets", 1e4, 1.0),   # four key groups
 ]
 
 

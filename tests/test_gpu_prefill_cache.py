@@ -69,7 +69,8 @@ def test_prefill_cache_parity(B, Sq, Hq, Hkv, D, max_kv, lens, causal, window, d
 
 @pytest.mark.parametrize("B,Sq,Hq,Hkv,D,lens,window", [
     (2, 2048, 64, 8, 128, [4096, 3000], 0),      # 8-wave kernel, chunk against a long context
-    (2, 2048, 64, 8, 128, [2048, 4000], 1024),   # 8-wave kernel, sliding window
+    (2, 2048, 64, 8, 128, [2048, 4000], 1024),   # 4-wave kernel, short sliding window
+    (2, 2048, 64, 8, 128, [2048, 4000], 2500),   # 8-wave kernel, sliding window
 ])
 def test_prefill_cache_large_sampled(B, Sq, Hq, Hkv, D, lens, window):
     announce(f"prefill_cache large B={B} Sq={Sq} Hq={Hq} lens={lens} window={window}")

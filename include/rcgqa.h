@@ -19,7 +19,9 @@
  *     allocates nothing, frees nothing and keeps no mutable global state.
  *   - Tensors are dense and row-major with head_dim innermost.  Element type is
  *     selected by `dt`: RCGQA_BF16 (bfloat16 storage, fp32 arithmetic) or
- *     RCGQA_FP32.
+ *     RCGQA_FP32.  Tensor pointers must be 16-byte aligned (the kernels move
+ *     16-byte vectors) and int32 arrays 4-byte aligned; any device allocator's
+ *     blocks are.  A misaligned pointer is RCGQA_EINVAL.
  *   - Every call is asynchronous on `stream` (a hipStream_t; NULL = the null
  *     stream).  Nothing synchronises inside the library.
  *   - Errors: every argument that can be checked on the host is checked before
@@ -78,6 +80,28 @@ rcgqa_status rope_apply(void* q, void* k, const int32_t* position_ids,
                         int B, int S, int Hq, int Hkv, int head_dim,
                         float theta, float linear_factor,
                         rcgqa_dtype dt, rcgqa_stream stream);
+
+/*
+ * rope_apply_interleaved -- rope_apply with adjacent pairs.
+ *
+ * Defines: the same rotation as rope_apply ([L2] "Rotary Position Encoding";
+ * [L2X] sections 2.1 and 6.1), with the pairing of its complex-number form
+ * ([L2X] section 2.1 calls it a rotation in the complex domain): element pair
+ * i is (x[2i], x[2i+1]), i.e. a fixed permutation of the head dimension away
+ * from rope_apply's (x[i], x[i+head_dim/2]).
+ *
+ *   pair i of every head vector, i in [0, head_dim/2), is (x[2i], x[2i+1])
+ *   angle = (pos / linear_factor) * theta^(-2 i / head_dim)
+ *   (x1, x2) <- (x1 cos(angle) - x2 sin(angle), x2 cos(angle) + x1 sin(angle))
+ *
+ * Arguments, layouts, precision and errors exactly as rope_apply; for every
+ * pair the angle, cos/sin and arithmetic are rope_apply's, so permuting the
+ * head dimension maps one result onto the other bit for bit.
+ */
+rcgqa_status rope_apply_interleaved(void* q, void* k, const int32_t* position_ids,
+                                    int B, int S, int Hq, int Hkv, int head_dim,
+                                    float theta, float linear_factor,
+                                    rcgqa_dtype dt, rcgqa_stream stream);
 
 /*
  * attn_prefill -- full-sequence scaled-dot-product attention, grouped-query.

@@ -7,9 +7,11 @@ it never computes any step itself.  The library is loaded on first use and a
 missing or unloadable library raises immediately.
 """
 from ._binding import (RcgqaError, attn_decode, attn_decode_workspace_bytes, attn_prefill,
-                       attn_prefill_cache, kv_append, lib, lib_path, rope_apply, rope_attn_decode,
-                       rope_attn_decode_workspace_bytes, rope_attn_prefill, rope_attn_prefill_workspace_bytes)
+                       attn_prefill_cache, kv_append, lib, lib_path, rope_apply, rope_apply_interleaved,
+                       rope_attn_decode, rope_attn_decode_workspace_bytes, rope_attn_prefill,
+                       rope_attn_prefill_workspace_bytes)
 
 __all__ = ["RcgqaError", "attn_decode", "attn_decode_workspace_bytes", "attn_prefill",
-           "attn_prefill_cache", "kv_append", "lib", "lib_path", "rope_apply", "rope_attn_decode",
-           "rope_attn_decode_workspace_bytes", "rope_attn_prefill", "rope_attn_prefill_workspace_bytes"]
+           "attn_prefill_cache", "kv_append", "lib", "lib_path", "rope_apply", "rope_apply_interleaved",
+           "rope_attn_decode", "rope_attn_decode_workspace_bytes", "rope_attn_prefill",
+           "rope_attn_prefill_workspace_bytes"]

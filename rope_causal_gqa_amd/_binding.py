@@ -38,6 +38,8 @@ def lib():
     vp, i32, f32, sz = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
     L.rope_apply.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, i32, vp]
     L.rope_apply.restype = i32
+    L.rope_apply_interleaved.argtypes = [vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, i32, vp]
+    L.rope_apply_interleaved.restype = i32
     L.attn_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_prefill.restype = i32
     L.attn_prefill_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
@@ -108,18 +110,27 @@ def _stream(t):
     return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
 
 
-def rope_apply(q, k, position_ids=None, theta=10000.0, linear_factor=1.0):
-    """Rotate q [B,S,Hq,D] and k [B,S,Hkv,D] in place (see rcgqa.h)."""
+def _rope(name, q, k, position_ids, theta, linear_factor):
     dt = _dtype_code(q)
     B, S, Hq, D = q.shape
     Hkv = k.shape[2]
     if tuple(k.shape) != (B, S, Hkv, D):
         raise ValueError(f"k shape {tuple(k.shape)} does not match q {tuple(q.shape)}")
     pos = ctypes.c_void_p(0) if position_ids is None else _i32(position_ids, "position_ids", B * S)
-    st = lib().rope_apply(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), pos, B, S, Hq, Hkv, D,
-                          float(theta), float(linear_factor), dt, _stream(q))
-    _check(st, "rope_apply")
+    st = getattr(lib(), name)(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), pos, B, S, Hq, Hkv, D,
+                              float(theta), float(linear_factor), dt, _stream(q))
+    _check(st, name)
     return q, k
+
+
+def rope_apply(q, k, position_ids=None, theta=10000.0, linear_factor=1.0):
+    """Rotate q [B,S,Hq,D] and k [B,S,Hkv,D] in place, pairs (x[i], x[i+D/2]) (see rcgqa.h)."""
+    return _rope("rope_apply", q, k, position_ids, theta, linear_factor)
+
+
+def rope_apply_interleaved(q, k, position_ids=None, theta=10000.0, linear_factor=1.0):
+    """Rotate q and k in place with adjacent pairs (x[2i], x[2i+1]) (see rcgqa.h)."""
+    return _rope("rope_apply_interleaved", q, k, position_ids, theta, linear_factor)
 
 
 def attn_prefill(q, k, v, out=None, causal=True, scale=None):

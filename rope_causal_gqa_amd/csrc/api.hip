@@ -15,6 +15,14 @@ constexpr int64_t kI32Max = 2147483647;
 bool pos_int(int x) { return x >= 1; }
 bool good_dtype(rcgqa_dtype dt) { return dt == RCGQA_BF16 || dt == RCGQA_FP32; }
 bool finite_pos(float x) { return std::isfinite(x) && x > 0.f; }
+// Tensors are accessed in 16-byte vectors (and 16-byte direct-to-LDS loads),
+// int32 arrays element-wise; null pointers pass here and are rejected apart.
+bool al16(std::initializer_list<const void*> ps) {
+  for (const void* p : ps)
+    if (reinterpret_cast<uintptr_t>(p) & 15) return false;
+  return true;
+}
+bool al4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3) == 0; }
 
 // Product of positive ints, or -1 on int64 overflow.
 int64_t mul(std::initializer_list<int64_t> xs) {
@@ -30,6 +38,19 @@ int64_t mul(std::initializer_list<int64_t> xs) {
 bool attn_head_dim(int d) { return d == 64 || d == 128; }
 
 rcgqa_status hip_status(hipError_t e) { return e == hipSuccess ? RCGQA_OK : RCGQA_EHIP; }
+
+// Host checks shared by the two pairings of the rotation.
+rcgqa_status rope_check(const void* q, const void* k, int B, int S, int Hq, int Hkv, int head_dim, float theta,
+                        float linear_factor, rcgqa_dtype dt) {
+  if (!q || !k || !good_dtype(dt) || !al16({q, k})) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2) return RCGQA_EINVAL;
+  if (!finite_pos(theta) || !finite_pos(linear_factor)) return RCGQA_EINVAL;
+  const int64_t tokens = mul({B, S});
+  if (tokens < 0 || tokens > kI32Max || mul({tokens, Hq, head_dim}) < 0) return RCGQA_EINVAL;
+  if (head_dim > 256) return RCGQA_EUNSUPPORTED;
+  return RCGQA_OK;
+}
 
 }  // namespace
 
@@ -47,20 +68,26 @@ const char* rcgqa_status_string(rcgqa_status s) {
 
 rcgqa_status rope_apply(void* q, void* k, const int32_t* position_ids, int B, int S, int Hq, int Hkv,
                         int head_dim, float theta, float linear_factor, rcgqa_dtype dt, rcgqa_stream stream) {
-  if (!q || !k || !good_dtype(dt)) return RCGQA_EINVAL;
-  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
-  if (head_dim < 2 || head_dim % 2) return RCGQA_EINVAL;
-  if (!finite_pos(theta) || !finite_pos(linear_factor)) return RCGQA_EINVAL;
-  const int64_t tokens = mul({B, S});
-  if (tokens < 0 || tokens > kI32Max || mul({tokens, Hq, head_dim}) < 0) return RCGQA_EINVAL;
-  if (head_dim > 256) return RCGQA_EUNSUPPORTED;
+  const rcgqa_status bad = rope_check(q, k, B, S, Hq, Hkv, head_dim, theta, linear_factor, dt);
+  if (bad != RCGQA_OK) return bad;
+  if (!al4(position_ids)) return RCGQA_EINVAL;
   return hip_status(rcgqa::launch_rope(q, k, position_ids, B, S, Hq, Hkv, head_dim, (double)theta,
                                        (double)linear_factor, dt == RCGQA_BF16, nullptr, (hipStream_t)stream));
 }
 
+rcgqa_status rope_apply_interleaved(void* q, void* k, const int32_t* position_ids, int B, int S, int Hq, int Hkv,
+                                    int head_dim, float theta, float linear_factor, rcgqa_dtype dt,
+                                    rcgqa_stream stream) {
+  const rcgqa_status bad = rope_check(q, k, B, S, Hq, Hkv, head_dim, theta, linear_factor, dt);
+  if (bad != RCGQA_OK) return bad;
+  if (!al4(position_ids)) return RCGQA_EINVAL;
+  return hip_status(rcgqa::launch_rope_interleaved(q, k, position_ids, B, S, Hq, Hkv, head_dim, (double)theta,
+                                                   (double)linear_factor, dt == RCGQA_BF16, (hipStream_t)stream));
+}
+
 rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq, int Hkv,
                           int head_dim, int causal, float scale, rcgqa_dtype dt, rcgqa_stream stream) {
-  if (!q || !k || !v || !out || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!q || !k || !v || !out || !good_dtype(dt) || !al16({q, k, v, out})) return RCGQA_EINVAL;
   if (out == q || out == k || out == v) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
@@ -80,6 +107,7 @@ rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* 
                                 void* out, int B, int Sq, int Hq, int Hkv, int head_dim, int max_kv, int causal,
                                 int window, float scale, rcgqa_dtype dt, rcgqa_stream stream) {
   if (!q || !k_cache || !v_cache || !kv_lens || !out || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!al16({q, k_cache, v_cache, out}) || !al4(kv_lens)) return RCGQA_EINVAL;
   if (out == q || out == k_cache || out == v_cache) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(Sq) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv))
     return RCGQA_EINVAL;
@@ -110,6 +138,7 @@ rcgqa_status rope_attn_prefill(const void* q, void* k, const void* v, void* out,
                                float linear_factor, rcgqa_dtype dt, void* workspace, size_t workspace_bytes,
                                rcgqa_stream stream) {
   if (!q || !k || !v || !out || !workspace || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!al16({q, k, v, out}) || !al4(position_ids)) return RCGQA_EINVAL;
   if (out == q || out == k || out == v || q == k || k == v) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
@@ -142,6 +171,7 @@ rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache
                          void* out, int B, int Hq, int Hkv, int head_dim, int max_kv, float scale,
                          rcgqa_dtype dt, void* workspace, size_t workspace_bytes, rcgqa_stream stream) {
   if (!q || !k_cache || !v_cache || !kv_lens || !out || !workspace || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!al16({q, k_cache, v_cache, out}) || !al4(kv_lens)) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
   if (B > 65535 || Hq > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
@@ -165,6 +195,7 @@ rcgqa_status rope_attn_decode(const void* q, const void* k_new, const void* v_ne
                               rcgqa_dtype dt, void* workspace, size_t workspace_bytes, rcgqa_stream stream) {
   if (!q || !k_new || !v_new || !k_cache || !v_cache || !kv_lens || !out || !workspace || !good_dtype(dt))
     return RCGQA_EINVAL;
+  if (!al16({q, k_new, v_new, k_cache, v_cache, out}) || !al4(kv_lens) || !al4(position_ids)) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
   if (!finite_pos(theta) || !finite_pos(linear_factor)) return RCGQA_EINVAL;
@@ -189,6 +220,7 @@ rcgqa_status rope_attn_decode(const void* q, const void* k_new, const void* v_ne
 rcgqa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const void* v_new, const int32_t* slots,
                        int B, int Hkv, int head_dim, int max_kv, rcgqa_dtype dt, rcgqa_stream stream) {
   if (!k_cache || !v_cache || !k_new || !v_new || !slots || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!al16({k_cache, v_cache, k_new, v_new}) || !al4(slots)) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(Hkv) || !pos_int(max_kv) || head_dim < 2 || head_dim % 2) return RCGQA_EINVAL;
   if (B > 65535 || Hkv > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
   if (head_dim > 256) return RCGQA_EUNSUPPORTED;

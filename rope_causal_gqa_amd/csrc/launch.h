@@ -24,6 +24,9 @@ struct KvSpec {
 // token's fp32 cos/sin row ([B*S, D]: cos of pairs 0..D/2-1, then sin).
 hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
                        double theta, double factor, bool bf16, float* table, hipStream_t st);
+// Same contract with the interleaved pairing (x[2i], x[2i+1]).
+hipError_t launch_rope_interleaved(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
+                                  double theta, double factor, bool bf16_io, hipStream_t st);
 
 // One decode step: rotate q into q_out and k_new at position pos[b] (kv_lens[b] - 1 when pos is null),
 // append the rotated key and v_new at row kv_lens[b] - 1 of the caches.

@@ -12,6 +12,10 @@
 // halves of a head vector, so loads and stores are fully coalesced.  The pass
 // is HBM-bound: it reads and writes every q/k element once.
 //
+// The interleaved pairing (x[2i], x[2i+1]) -- the complex-pair form of the
+// same rotation -- has its own kernel: each 16-byte vector then holds whole
+// pairs, with the same angles and arithmetic per pair.
+//
 // For the fused paths the same kernel can rotate K alone and write the
 // token's cos/sin row to a table (the prefill kernel then rotates Q as it
 // loads it, with the very same values and arithmetic), and a second kernel
@@ -81,6 +85,37 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
   }
 }
 
+// Interleaved pairs: VE elements (VE/2 whole pairs) per vector, pair i of a
+// head vector is (x[2i], x[2i+1]) with the angle of frequency index i.
+template <typename T, int VE>
+__global__ __launch_bounds__(256) void rope_interleaved_kernel(T* __restrict__ q, T* __restrict__ k,
+                                                               const int32_t* __restrict__ pos_ids, int S, int Hq,
+                                                               int Hkv, int D, double theta, double factor) {
+  extern __shared__ float cs[];  // cos[D/2] then sin[D/2]
+  const int tok = blockIdx.x;
+  const int half = D >> 1;
+  const int pos = pos_ids ? pos_ids[tok] : (tok % S);
+  rope_angles(cs, pos, D, theta, factor);
+  __syncthreads();
+  const int cpr = D / VE;  // vectors per head vector
+  const int units = (Hq + Hkv) * cpr;
+  for (int u = threadIdx.x; u < units; u += blockDim.x) {
+    const int head = u / cpr, c = u - head * cpr;
+    T* p = (head < Hq ? q + ((size_t)tok * Hq + head) * D : k + ((size_t)tok * Hkv + (head - Hq)) * D) + c * VE;
+    const Vec<T, VE> x = *reinterpret_cast<const Vec<T, VE>*>(p);
+    Vec<T, VE> y;
+#pragma unroll
+    for (int j = 0; j < VE / 2; j++) {
+      const int i = c * (VE / 2) + j;
+      const float co = cs[i], si = cs[half + i];
+      const float a = (float)x.v[2 * j], b = (float)x.v[2 * j + 1];
+      y.v[2 * j] = (T)fmaf(a, co, -(b * si));
+      y.v[2 * j + 1] = (T)fmaf(b, co, a * si);
+    }
+    *reinterpret_cast<Vec<T, VE>*>(p) = y;
+  }
+}
+
 // One decode step per sequence b (one workgroup each): rotate q[b] into
 // q_out[b] and k_new[b] at position pos_b, then write the rotated key and
 // v_new[b] into cache row slot_b = kv_lens[b] - 1 (nothing is written when
@@ -141,6 +176,28 @@ hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int H
     else
       hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, lds, st, (float*)q, (float*)k, pos, S, Hq, Hkv,
                          D, theta, factor, table);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_rope_interleaved(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
+                                  double theta, double factor, bool bf16_io, hipStream_t st) {
+  const dim3 grid((unsigned)((long)B * S)), block(256);
+  const size_t lds = (size_t)D * sizeof(float);
+  if (bf16_io) {
+    if (D % 8 == 0)
+      hipLaunchKernelGGL((rope_interleaved_kernel<bf16, 8>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq,
+                         Hkv, D, theta, factor);
+    else
+      hipLaunchKernelGGL((rope_interleaved_kernel<bf16, 2>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq,
+                         Hkv, D, theta, factor);
+  } else {
+    if (D % 4 == 0)
+      hipLaunchKernelGGL((rope_interleaved_kernel<float, 4>), grid, block, lds, st, (float*)q, (float*)k, pos, S,
+                         Hq, Hkv, D, theta, factor);
+    else
+      hipLaunchKernelGGL((rope_interleaved_kernel<float, 2>), grid, block, lds, st, (float*)q, (float*)k, pos, S,
+                         Hq, Hkv, D, theta, factor);
   }
   return hipGetLastError();
 }

@@ -23,7 +23,7 @@ def _declared():
 
 def test_exports_every_declared_symbol():
     names = _declared()
-    assert set(names) >= {"rope_apply", "attn_prefill", "attn_prefill_cache", "attn_decode",
+    assert set(names) >= {"rope_apply", "rope_apply_interleaved", "attn_prefill", "attn_prefill_cache", "attn_decode",
                           "attn_decode_workspace_bytes", "kv_append", "rcgqa_status_string"}
     L = R.lib()
     for n in names:
@@ -60,16 +60,18 @@ FAKE = ctypes.c_void_p(4096)   # never dereferenced: every call below fails vali
     dict(D=63), dict(D=0), dict(theta=0.0), dict(theta=float("inf")), dict(factor=0.0),
     dict(factor=float("nan")), dict(dt=7),
 ])
-def test_rope_rejects(args):
+@pytest.mark.parametrize("name", ["rope_apply", "rope_apply_interleaved"])
+def test_rope_rejects(args, name):
     a = dict(q=FAKE, k=FAKE, B=1, S=4, Hq=8, Hkv=2, D=64, theta=1e4, factor=1.0, dt=0)
     a.update(args)
-    st = R.lib().rope_apply(a["q"], a["k"], None, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["theta"],
-                            a["factor"], a["dt"], None)
+    st = getattr(R.lib(), name)(a["q"], a["k"], None, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["theta"],
+                                a["factor"], a["dt"], None)
     assert st == BD.EINVAL
 
 
-def test_rope_unsupported_head_dim():
-    assert R.lib().rope_apply(FAKE, FAKE, None, 1, 1, 1, 1, 258, 1e4, 1.0, 0, None) == BD.EUNSUPPORTED
+@pytest.mark.parametrize("name", ["rope_apply", "rope_apply_interleaved"])
+def test_rope_unsupported_head_dim(name):
+    assert getattr(R.lib(), name)(FAKE, FAKE, None, 1, 1, 1, 1, 258, 1e4, 1.0, 0, None) == BD.EUNSUPPORTED
 
 
 @pytest.mark.parametrize("args", [
@@ -135,6 +137,28 @@ def test_kv_append_rejects():
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 4, 0, None) == BD.EINVAL
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 63, 4, 0, None) == BD.EINVAL
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, 1, 1, 64, 0, 0, None) == BD.EINVAL
+
+
+MIS = ctypes.c_void_p(4096 + 2)   # not 16-byte (nor 4-byte) aligned
+A = [ctypes.c_void_p(4096 * i) for i in range(1, 9)]
+WS = ctypes.c_void_p(4096 * 64)
+
+
+@pytest.mark.parametrize("call", [
+    lambda L: L.rope_apply(MIS, A[1], None, 1, 4, 8, 2, 64, 1e4, 1.0, 0, None),
+    lambda L: L.rope_apply_interleaved(A[0], MIS, None, 1, 4, 8, 2, 64, 1e4, 1.0, 0, None),
+    lambda L: L.rope_apply(A[0], A[1], MIS, 1, 4, 8, 2, 64, 1e4, 1.0, 0, None),
+    lambda L: L.attn_prefill(A[0], A[1], MIS, A[3], 1, 4, 8, 2, 64, 1, 0.125, 0, None),
+    lambda L: L.attn_prefill_cache(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 16, 1, 0, 0.125, 0, None),
+    lambda L: L.attn_decode(A[0], MIS, A[2], A[3], A[4], 1, 8, 2, 128, 16, 0.1, 0, WS, 1 << 30, None),
+    lambda L: L.rope_attn_prefill(A[0], A[1], A[2], MIS, None, 1, 16, 8, 2, 64, 1, 0.125, 1e4, 1.0, 0, WS, 1 << 20,
+                                  None),
+    lambda L: L.rope_attn_decode(A[0], A[1], MIS, A[3], A[4], A[5], None, A[6], 1, 8, 2, 128, 16, 0.1, 1e4, 1.0, 0,
+                                 WS, 1 << 30, None),
+    lambda L: L.kv_append(A[0], A[1], MIS, A[3], A[4], 1, 2, 64, 16, 0, None),
+])
+def test_misaligned_pointers_rejected(call):
+    assert call(R.lib()) == BD.EINVAL
 
 
 def test_binding_requires_device_tensors():

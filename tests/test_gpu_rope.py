@@ -1,4 +1,4 @@
-"""rope_apply on the GPU against the float64 oracle."""
+"""rope_apply and rope_apply_interleaved on the GPU against the float64 oracle."""
 import numpy as np
 import pytest
 
@@ -60,3 +60,42 @@ def test_rope_fp32_long_positions():
     k = W.random_case(6, (1, 8, 1, 128), "fp32")
     pos = np.array([[0, 1, 127, 4095, 8192, 65535, 1 << 20, 2_000_000_000]], dtype=np.int32)
     _run(q, k, pos, 10000.0, 1.0, "fp32", "rope fp32 long positions")
+
+
+def _run_interleaved(q, k, pos, theta, factor, dtype, what):
+    import torch
+    announce(what)
+    qd, kd = dev(q, dtype), dev(k, dtype)
+    pd = None if pos is None else torch.from_numpy(np.ascontiguousarray(pos, dtype=np.int32)).cuda()
+    R.rope_apply_interleaved(qd, kd, pd, theta, factor)
+    torch.cuda.synchronize()
+    qr, kr = oracle.rope_apply(W.to_f64(q, dtype), W.to_f64(k, dtype), pos, theta, factor, style="interleaved")
+    check(host64(qd), qr, dtype, what + " q")
+    check(host64(kd), kr, dtype, what + " k")
+    return qd, kd, pd
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [2, 6, 64, 128, 256])
+def test_rope_interleaved_head_dims(dtype, D):
+    """Adjacent pairs against the oracle's interleaved rotation, and bit for bit
+    against rope_apply on the head dimension permuted so that pair i = (2i, 2i+1)
+    becomes (i, i + D/2)."""
+    import torch
+    B, S, Hq, Hkv = 2, 33, 4, 2
+    q = W.random_case(7 * D, (B, S, Hq, D), dtype)
+    k = W.random_case(7 * D + 1, (B, S, Hkv, D), dtype)
+    pos = np.random.Generator(np.random.PCG64(3 * D)).integers(-50, 9000, size=(B, S)).astype(np.int32)
+    qi, ki, pd = _run_interleaved(q, k, pos, 500000.0, 4.0, dtype, f"rope interleaved D={D} {dtype}")
+    perm = torch.cat([torch.arange(0, D, 2), torch.arange(1, D, 2)]).cuda()  # interleaved -> half-split order
+    qh, kh = dev(q, dtype)[..., perm].contiguous(), dev(k, dtype)[..., perm].contiguous()
+    R.rope_apply(qh, kh, pd, 500000.0, 4.0)
+    inv = torch.argsort(perm)
+    torch.cuda.synchronize()
+    assert torch.equal(qh[..., inv], qi) and torch.equal(kh[..., inv], ki)
+
+
+def test_rope_interleaved_c3_full_size():
+    w = W.WORKLOADS["c3"]
+    q, k, _ = W.prefill_inputs(w)
+    _run_interleaved(q, k, None, w.theta, w.factor, "bf16", "rope interleaved c3 full")

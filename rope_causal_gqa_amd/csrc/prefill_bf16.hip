@@ -6,11 +6,14 @@
 // weights @ V; query head h reads K/V head h / G (repeat_kv).
 //
 // Design (one workgroup = NW waves = 32 NW query rows of one (batch, head);
-// NW = 8 when the grid is large enough, else 4):
-//  * K/V tiles of 64 keys are double-buffered in LDS and filled with direct
-//    global->LDS loads (buffer / global load ... lds) one tile ahead of the math,
-//    with a row-dependent XOR swizzle of 16-byte chunks so all three read
-//    patterns below are bank-conflict free.  One barrier per tile.
+// NW = 8 when the grid is large enough, else 4; grids too small for that run
+// one 8-wave workgroup per CU split into two or four key groups, see the
+// launcher):
+//  * K/V tiles of 64 keys (32 with four key groups) are double-buffered in
+//    LDS and filled with direct global->LDS loads (buffer / global load ...
+//    lds) one tile ahead of the math, with a row-dependent XOR swizzle of
+//    16-byte chunks so all three read patterns below are bank-conflict free.
+//    One barrier per tile.
 //  * Scores are formed transposed, S^T = K Q^T, with v_mfma_f32_32x32x16_bf16:
 //    K rows are the A operand (read straight from LDS), the wave's 32 query
 //    rows are the B operand (held in registers for the whole kernel).  In the

@@ -41,11 +41,10 @@
 //    the first tile ("LLaMA2大语言模型架构详解", section "Rotary Position
 //    Encoding"), so the queries never make a separate pass through memory.
 #include <algorithm>
-#include <functional>
-#include <vector>
 #include <type_traits>
 
 #include "common.h"
+#include "grid_model.h"
 #include "launch.h"
 
 namespace rcgqa {
@@ -472,77 +471,15 @@ static void launch_nw(const void* q, const void* k, const void* v, void* out, in
 }
 
 namespace {
-constexpr int kCUs = 256;  // compute units of a gfx950 MI355X
-
-// sum over query rows i in [a, b) of min(max(i + c, 0), cap): the keys those rows see
-double rows_keys(long long a, long long b, long long c, long long cap) {
-  const long long z = std::min(std::max(a, 1 - c), b);    // first row that sees a key
-  const long long u = std::min(std::max(z, cap - c), b);  // first row that sees cap keys
-  return 0.5 * (double)(u - z) * (double)(z + c + u - 1 + c) + (double)(b - u) * (double)cap;
-}
-
-// Finish time of the busiest CU for a grid of
-// bh * w.size() workgroups (work item i = head i / w.size(), slot i % w.size(),
-// taking time w[slot]) that run one per CU: each XCD takes its share of the
-// work list (see the kernel's work mapping) in order and hands every item to
-// whichever of its CUs frees first.
-double busiest_cu(const std::vector<double>& w, long long bh) {
-  const long long n = bh * (long long)w.size();
-  const int per_xcd = kCUs / 8;
-  double worst = 0;
-  std::vector<double> load(per_xcd);
-  for (int x = 0; x < 8; x++) {
-    std::fill(load.begin(), load.end(), 0.0);  // a min-heap of this XCD's CU loads
-    auto take = [&](long long item) {
-      std::pop_heap(load.begin(), load.end(), std::greater<double>());
-      load.back() += w[item % (long long)w.size()];
-      std::push_heap(load.begin(), load.end(), std::greater<double>());
-    };
-    if (n % 8 == 0)
-      for (long long i = x * (n / 8); i < (x + 1) * (n / 8); i++) take(i);
-    else
-      for (long long i = x; i < n; i += 8) take(i);
-    worst = std::max(worst, *std::max_element(load.begin(), load.end()));
-  }
-  return worst;
-}
-
-// For query counts too small for 512 workgroups of 4 waves there are two
-// grids: 128-row tiles in two key groups (A) and 64-row tiles in four key
-// groups over 32-key K/V tiles (B, causal tiles paired when that keeps 256
-// workgroups).  B cuts the work finer; A moves half the K/V tile traffic per
-// flop, runs 64-key steps and sets up one tile per workgroup.  Each grid's
-// workgroup time is modelled as a set-up cost per query tile plus its
-// (query row, key) pairs over a rate, both fitted to MI355X timings of the
-// two kernels (A: 3.1 us + pairs / 7.3e3 per us; B: 7.5 us per tile + pairs
-// / 6.1e3 per us), and B is taken when it is estimated to finish first.
-// Rows see keys by the causal and window rules, caches taken as full.
-bool four_groups_model(long long bh, int Sq, bool causal, const KvSpec& kv, int nqt2, int npairs2, int nqt4) {
-  constexpr double kSetupA = 3.1, kRateA = 7.3e3, kSetupB = 7.5, kRateB = 6.1e3;
-  const long long nk = kv.lens ? kv.max_kv : Sq;
-  const long long c = causal ? nk - Sq + 1 : nk, cap = kv.window > 0 ? std::min<long long>(kv.window, nk) : nk;
-  // heavy (late) tiles first, as the kernel orders them
-  std::vector<double> wa(nqt4), wb(npairs2);
-  for (int t = 0; t < nqt4; t++) {
-    const int qt = causal ? nqt4 - 1 - t : t;
-    wa[t] = kSetupA + rows_keys(128LL * qt, std::min(128LL * qt + 128, (long long)Sq), c, cap) / kRateA;
-  }
-  auto w2 = [&](int qt) { return kSetupB + rows_keys(64LL * qt, std::min(64LL * qt + 64, (long long)Sq), c, cap) / kRateB; };
-  for (int p = 0; p < npairs2; p++) {
-    const int qt = causal ? nqt2 - 1 - p : p;
-    wb[p] = w2(qt) + (npairs2 < nqt2 && p != qt ? w2(p) : 0.0);
-  }
-  return busiest_cu(wb, bh) < busiest_cu(wa, bh);
-}
-
 // The choice for the last shape seen on this thread is kept: serving loops
 // repeat shapes, and the estimate walks every workgroup of both grids.
-bool four_groups_first(long long bh, int Sq, bool causal, const KvSpec& kv, int nqt2, int npairs2, int nqt4) {
+grid::KeyGroupGrid key_group_grid_cached(long long bh, int Sq, bool causal, const KvSpec& kv) {
+  const long long nk = kv.lens ? kv.max_kv : Sq;
   const long long key[5] = {bh, Sq, causal, kv.lens ? kv.max_kv : -1, kv.window};
   thread_local long long last[5] = {-1, -1, -1, -1, -1};
-  thread_local bool last_choice = false;
+  thread_local grid::KeyGroupGrid last_choice{false, 0};
   if (!std::equal(key, key + 5, last)) {
-    last_choice = four_groups_model(bh, Sq, causal, kv, nqt2, npairs2, nqt4);
+    last_choice = grid::key_group_grid(bh, Sq, causal, nk, kv.window);
     std::copy(key, key + 5, last);
   }
   return last_choice;
@@ -574,15 +511,14 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   } else {
     const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;
     const int npairs = pair4 ? (nqt4 + 1) / 2 : nqt4;
-    const int nqt2 = (Sq + 63) / 64;
     if (bh * npairs >= 512) {
       launch_nw<4, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
     } else {
-      const int npairs2 = causal && nqt2 > 1 && bh * ((nqt2 + 1) / 2) >= 256 ? (nqt2 + 1) / 2 : nqt2;
-      if (four_groups_first(bh, Sq, causal, kv, nqt2, npairs2, nqt4))
-        launch_nw<8, 4, 32>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs2, kv, q_rope, st);
+      const grid::KeyGroupGrid g = key_group_grid_cached(bh, Sq, causal, kv);
+      if (g.four)
+        launch_nw<8, 4, 32>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, g.npairs, kv, q_rope, st);
       else
-        launch_nw<8, 2>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, nqt4, kv, q_rope, st);
+        launch_nw<8, 2>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, g.npairs, kv, q_rope, st);
     }
   }
   return hipGetLastError();

@@ -15,6 +15,7 @@ blocking, fusion or reordering beyond that definition:
                    prefill against a cache.
 * ``fused``     -- rotation then attention, as one prefill or one decode step
                    (with the cache append), composed from the two above.
+* ``ntk``       -- NTK-aware scaling of the RoPE base (static and dynamic).
 
 Pins (tests marked ``not gpu``) tie each function to something other than
 itself: closed forms, invariants, brute-force loops on tiny shapes, a library
@@ -24,7 +25,8 @@ and hand-derived fixtures under ``tests/golden``.
 from .rope import inv_freq, angles, rotate, rope_apply
 from .attention import attention, attention_cache, attention_probs, decode, kv_append
 from .fused import rope_attention, rope_decode_step
+from .ntk import ntk_theta, dynamic_ntk_theta
 
 __all__ = ["inv_freq", "angles", "rotate", "rope_apply",
            "attention", "attention_cache", "attention_probs", "decode", "kv_append",
-           "rope_attention", "rope_decode_step"]
+           "rope_attention", "rope_decode_step", "ntk_theta", "dynamic_ntk_theta"]

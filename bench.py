@@ -19,7 +19,8 @@ time the two prefill extensions (attn_prefill_cache) separately, after the
 timed steps; `gqa_prefill` times attn_prefill on the LLaMA-70B-shaped GQA
 prefill (B=1 S=4096 Hq=64 Hkv=8 D=128) and on its 8-query-head / 1-KV-head
 share; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
-entry points against the separate calls on the same workloads.  `cpu_baseline` times the float64 oracle on a bounded sample on
+entry points against the separate calls on the same workloads; `ntk_rope`
+times rope_apply at an NTK-aware scaled base.  `cpu_baseline` times the float64 oracle on a bounded sample on
 the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
@@ -186,7 +187,15 @@ def _fused_rows(R, wp, wd, q, k, v, out, dq, dkn, dvn, kc, vc, ctx_d, lens_d, po
         R.kv_append(kc, vc, dkn3, dvn, ctx_d)
         R.attn_decode(dq3, kc, vc, lens_d, dout, scale=wd.scale, workspace=ws)
     dsep_ms = _time_launches(dsep, stream)
+    # NTK-aware scaling only changes the base handed to the RoPE kernel
+    ntk_theta = R.rope_ntk_theta(wp.theta, wp.D, 8.0)
+    ntk_ms = _time_launches(lambda: R.rope_apply(q, k, None, ntk_theta, 1.0), stream)
+    rope_bytes = 2.0 * wp.B * wp.S * (wp.Hq + wp.Hkv) * wp.D * 2
     return {
+        "ntk_rope": {
+            "workload": f"rope_apply on the B=2 S=4096 Hq=Hkv=32 D=128 bf16 Q/K at the NTK-aware base for scale 8 "
+                        f"(theta {ntk_theta:.1f})",
+            "value": round(rope_bytes / (ntk_ms * 1e-3) / 1e9, 1), "unit": "GB/s", "launch_ms": round(ntk_ms, 4)},
         "fused_rope_prefill": {
             "workload": "B=2 S=4096 Hq=Hkv=32 D=128 bf16 causal, RoPE theta 1e4 + attention",
             "fused_ms": round(fused_ms, 4), "separate_ms": round(sep_ms, 4),
@@ -344,6 +353,7 @@ def main():
         "gqa_prefill": extras.get("gqa_prefill"),
         "fused_rope_prefill": fused.get("fused_rope_prefill"),
         "fused_rope_decode": fused.get("fused_rope_decode"),
+        "ntk_rope": fused.get("ntk_rope"),
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

@@ -104,6 +104,33 @@ rcgqa_status rope_apply_interleaved(void* q, void* k, const int32_t* position_id
                                     rcgqa_dtype dt, rcgqa_stream stream);
 
 /*
+ * rope_ntk_theta / rope_dynamic_ntk_theta -- the RoPE base for NTK-aware
+ * scaling (host-side arithmetic; nothing is launched).
+ *
+ * Defines: [L2X] section 6.1 names NTK-aware scaling, next to linear
+ * interpolation, as a way to extend RoPE past the trained length by adjusting
+ * the rotation angles; it prints no formula.  The definition taken is the
+ * published "NTK-aware scaled RoPE" one (2023; also the dynamic NTK rotary
+ * embedding of Hugging Face Transformers): positions are not divided, the base
+ * is raised instead so that the highest-frequency pair keeps its angle and
+ * the lowest-frequency pair is divided by the scale alpha:
+ *
+ *   theta_out = theta * alpha^(head_dim / (head_dim - 2))
+ *
+ * The dynamic form takes alpha = factor * seq_len / max_position - (factor - 1)
+ * when seq_len > max_position, and returns theta unchanged otherwise.  Pass
+ * theta_out (with linear_factor 1) to rope_apply or the fused entry points.
+ *
+ * theta > 0, finite; head_dim even, >= 4; alpha > 0, finite; factor > 0,
+ * finite; seq_len, max_position >= 1; theta_out non-null.  The value is
+ * formed in double and rounded once to float; a result that is not a finite
+ * float is RCGQA_EINVAL.
+ */
+rcgqa_status rope_ntk_theta(float theta, int head_dim, float alpha, float* theta_out);
+rcgqa_status rope_dynamic_ntk_theta(float theta, int head_dim, float factor, int seq_len,
+                                    int max_position, float* theta_out);
+
+/*
  * attn_prefill -- full-sequence scaled-dot-product attention, grouped-query.
  *
  * Defines: [HF] section 1.2 steps 2-4 and section 2 steps 4-5 (scores

@@ -60,6 +60,10 @@ def lib():
     L.rope_attn_decode.argtypes = [vp, vp, vp, vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, f32, f32, i32, vp,
                                    sz, vp]
     L.rope_attn_decode.restype = i32
+    L.rope_ntk_theta.argtypes = [f32, i32, f32, ctypes.POINTER(ctypes.c_float)]
+    L.rope_ntk_theta.restype = i32
+    L.rope_dynamic_ntk_theta.argtypes = [f32, i32, f32, i32, i32, ctypes.POINTER(ctypes.c_float)]
+    L.rope_dynamic_ntk_theta.restype = i32
     L.rcgqa_status_string.argtypes = [i32]
     L.rcgqa_status_string.restype = ctypes.c_char_p
     _lib = L
@@ -121,6 +125,21 @@ def _rope(name, q, k, position_ids, theta, linear_factor):
                               float(theta), float(linear_factor), dt, _stream(q))
     _check(st, name)
     return q, k
+
+
+def rope_ntk_theta(theta, head_dim, alpha):
+    """RoPE base for NTK-aware scaling by alpha (see rcgqa.h); pass it to rope_apply."""
+    out = ctypes.c_float()
+    _check(lib().rope_ntk_theta(float(theta), int(head_dim), float(alpha), ctypes.byref(out)), "rope_ntk_theta")
+    return out.value
+
+
+def rope_dynamic_ntk_theta(theta, head_dim, factor, seq_len, max_position):
+    """RoPE base of the dynamic NTK form for a sequence of seq_len tokens (see rcgqa.h)."""
+    out = ctypes.c_float()
+    _check(lib().rope_dynamic_ntk_theta(float(theta), int(head_dim), float(factor), int(seq_len), int(max_position),
+                                        ctypes.byref(out)), "rope_dynamic_ntk_theta")
+    return out.value
 
 
 def rope_apply(q, k, position_ids=None, theta=10000.0, linear_factor=1.0):

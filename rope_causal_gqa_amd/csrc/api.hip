@@ -85,6 +85,32 @@ rcgqa_status rope_apply_interleaved(void* q, void* k, const int32_t* position_id
                                                    (double)linear_factor, dt == RCGQA_BF16, (hipStream_t)stream));
 }
 
+rcgqa_status rope_ntk_theta(float theta, int head_dim, float alpha, float* theta_out) {
+  if (!theta_out || !finite_pos(theta) || !finite_pos(alpha) || head_dim < 4 || head_dim % 2) return RCGQA_EINVAL;
+  const double t = (double)theta * std::pow((double)alpha, (double)head_dim / (double)(head_dim - 2));
+  const float f = (float)t;
+  if (!finite_pos(f)) return RCGQA_EINVAL;
+  *theta_out = f;
+  return RCGQA_OK;
+}
+
+rcgqa_status rope_dynamic_ntk_theta(float theta, int head_dim, float factor, int seq_len, int max_position,
+                                    float* theta_out) {
+  if (!theta_out || !finite_pos(theta) || !finite_pos(factor) || head_dim < 4 || head_dim % 2) return RCGQA_EINVAL;
+  if (!pos_int(seq_len) || !pos_int(max_position)) return RCGQA_EINVAL;
+  if (seq_len <= max_position) {
+    *theta_out = theta;
+    return RCGQA_OK;
+  }
+  const double alpha = (double)factor * (double)seq_len / (double)max_position - ((double)factor - 1.0);
+  if (!(alpha > 0.0)) return RCGQA_EINVAL;
+  const double t = (double)theta * std::pow(alpha, (double)head_dim / (double)(head_dim - 2));
+  const float f = (float)t;
+  if (!finite_pos(f)) return RCGQA_EINVAL;
+  *theta_out = f;
+  return RCGQA_OK;
+}
+
 rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq, int Hkv,
                           int head_dim, int causal, float scale, rcgqa_dtype dt, rcgqa_stream stream) {
   if (!q || !k || !v || !out || !good_dtype(dt) || !al16({q, k, v, out})) return RCGQA_EINVAL;

@@ -233,3 +233,37 @@ def test_fused_binding_requires_device_tensors():
     with pytest.raises(ValueError):
         R.rope_attn_decode(torch.zeros(1, 2, 64), torch.zeros(1, 1, 64), torch.zeros(1, 1, 64),
                            torch.zeros(1, 1, 8, 64), torch.zeros(1, 1, 8, 64), torch.ones(1, dtype=torch.int32))
+
+
+@pytest.mark.parametrize("theta,D,alpha", [(1e4, 128, 8.0), (5e5, 64, 2.5), (1e4, 4, 4.0), (100.0, 256, 0.5),
+                                           (1e4, 128, 1.0)])
+def test_ntk_theta_matches_oracle(theta, D, alpha):
+    """Host-side arithmetic (nothing launched): the library's base against the
+    oracle's float64 one, to float rounding."""
+    import oracle
+    assert R.rope_ntk_theta(theta, D, alpha) == pytest.approx(oracle.ntk_theta(theta, D, alpha), rel=2 ** -23)
+
+
+@pytest.mark.parametrize("theta,D,f,L,L0", [(1e4, 128, 2.0, 8192, 4096), (1e4, 128, 2.0, 4096, 4096),
+                                            (1e4, 64, 4.0, 5000, 2048), (5e5, 128, 1.0, 100, 4096)])
+def test_dynamic_ntk_theta_matches_oracle(theta, D, f, L, L0):
+    import oracle
+    got = R.rope_dynamic_ntk_theta(theta, D, f, L, L0)
+    assert got == pytest.approx(oracle.dynamic_ntk_theta(theta, D, f, L, L0), rel=2 ** -23)
+    if L <= L0:
+        assert got == theta
+
+
+@pytest.mark.parametrize("args", [(0.0, 128, 2.0), (1e4, 2, 2.0), (1e4, 127, 2.0), (1e4, 128, 0.0),
+                                  (1e4, 128, float("nan")), (3e38, 128, 4.0)])
+def test_ntk_theta_rejects(args):
+    out = ctypes.c_float()
+    assert R.lib().rope_ntk_theta(*args, ctypes.byref(out)) == BD.EINVAL
+    assert R.lib().rope_ntk_theta(1e4, 128, 2.0, None) == BD.EINVAL
+
+
+@pytest.mark.parametrize("args", [(1e4, 128, 0.0, 8192, 4096), (1e4, 128, 2.0, 0, 4096), (1e4, 128, 2.0, 10, 0),
+                                  (1e4, 6, -1.0, 10, 4), (1e4, 3, 2.0, 10, 4)])
+def test_dynamic_ntk_theta_rejects(args):
+    out = ctypes.c_float()
+    assert R.lib().rope_dynamic_ntk_theta(*args, ctypes.byref(out)) == BD.EINVAL

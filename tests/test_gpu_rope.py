@@ -99,3 +99,23 @@ def test_rope_interleaved_c3_full_size():
     w = W.WORKLOADS["c3"]
     q, k, _ = W.prefill_inputs(w)
     _run_interleaved(q, k, None, w.theta, w.factor, "bf16", "rope interleaved c3 full")
+
+
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+def test_rope_ntk_scaled_base(dtype):
+    """NTK-aware scaling: rope_apply at the library's scaled base (static scale
+    8, and the dynamic form for an 8192-token sequence trained at 4096) against
+    the oracle's rotation at that base, positions past the trained length."""
+    import oracle as O
+    D = 128
+    rng = np.random.Generator(np.random.PCG64(41))
+    q = W.random_case(41, (2, 48, 4, D), dtype)
+    k = W.random_case(42, (2, 48, 2, D), dtype)
+    static = R.rope_ntk_theta(1e4, D, 8.0)
+    dynamic = R.rope_dynamic_ntk_theta(1e4, D, 2.0, 8192, 4096)
+    assert static == pytest.approx(O.ntk_theta(1e4, D, 8.0), rel=2 ** -23)
+    assert dynamic == pytest.approx(O.dynamic_ntk_theta(1e4, D, 2.0, 8192, 4096), rel=2 ** -23)
+    pos = rng.integers(4096, 32768, size=(2, 48)).astype(np.int32)
+    _run(q, k, pos, static, 1.0, dtype, f"rope NTK static scale 8 {dtype}")
+    pos = rng.integers(0, 8192, size=(2, 48)).astype(np.int32)
+    _run(q, k, pos, dynamic, 1.0, dtype, f"rope NTK dynamic 8192/4096 {dtype}")

@@ -6,8 +6,11 @@ section 1.2 steps 2-4 and section 2 forward steps 4-5):
 * scores = scale * Q K^T per head, with scale = 1/sqrt(d_k) by default and
   passed in by the caller (the ``scaling`` argument of the verl page, section
   "4.48+ 版本的主要区别");
-* an additive mask; here only the causal one, with -inf on masked entries so
-  they get exactly zero weight.  Alignment (a reading): query i of Sq sits at
+* an additive mask (section 1.2 step 3: the mask is sliced to the query and
+  key lengths and added to the scaled scores): the causal one, with -inf on
+  masked entries so they get exactly zero weight, and optionally a general
+  one given as an array [B, Hm, Sq, Sk] (Hm = 1: shared by all query heads,
+  Hm = Hq: one per head) added to the scaled scores as it is.  Alignment (a reading): query i of Sq sits at
   absolute position Sk - Sq + i, so it sees keys j <= i + (Sk - Sq); with
   Sq == Sk this is the usual lower triangle;
 * softmax over keys, then weights @ V;
@@ -81,24 +84,32 @@ def attention_probs(q, k, scale, causal, b, h):
     return _softmax_rows(_scores(q[b, :, h, :], k[b, :, h // G, :], scale, causal))
 
 
-def attention(q, k, v, causal, scale, heads=None, window=0):
+def attention(q, k, v, causal, scale, heads=None, window=0, mask=None):
     """out[b, i, h, :] = sum_j softmax_j(scale q_i.k_j + mask_ij) v_j.
 
     q [B,Sq,Hq,D], k/v [B,Sk,Hkv,D] (any float dtype; upcast to float64).
     ``heads`` optionally restricts the work to a list of (b, h) pairs; the
     other rows of the result are left as NaN.  ``window`` > 0 adds the
-    sliding window (causal only).
+    sliding window (causal only).  ``mask`` [B, Hm, Sq, Sk] (Hm = 1 or Hq), if
+    given, is added to the scaled scores on top of the causal mask.
     """
     q = np.asarray(q, dtype=np.float64)
     k = np.asarray(k, dtype=np.float64)
     v = np.asarray(v, dtype=np.float64)
     B, Sq, Hq, D, Sk, Hkv = _check(q, k, v)
     G = Hq // Hkv
+    if mask is not None:
+        mask = np.asarray(mask, dtype=np.float64)
+        if mask.ndim != 4 or mask.shape[0] != B or mask.shape[1] not in (1, Hq) or mask.shape[2:] != (Sq, Sk):
+            raise ValueError("mask must be [B, 1 or Hq, Sq, Sk]")
     out = np.full((B, Sq, Hq, D), np.nan)
     pairs = heads if heads is not None else [(b, h) for b in range(B) for h in range(Hq)]
     for b, h in pairs:
         kh = h // G
-        p = _softmax_rows(_scores(q[b, :, h, :], k[b, :, kh, :], scale, causal, window))
+        s = _scores(q[b, :, h, :], k[b, :, kh, :], scale, causal, window)
+        if mask is not None:
+            s = s + mask[b, h if mask.shape[1] > 1 else 0]
+        p = _softmax_rows(s)
         out[b, :, h, :] = p @ v[b, :, kh, :]
     return out
 

@@ -20,7 +20,8 @@ timed steps; `gqa_prefill` times attn_prefill on the LLaMA-70B-shaped GQA
 prefill (B=1 S=4096 Hq=64 Hkv=8 D=128) and on its 8-query-head / 1-KV-head
 share; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
 entry points against the separate calls on the same workloads; `ntk_rope`
-times rope_apply at an NTK-aware scaled base.  `cpu_baseline` times the float64 oracle on a bounded sample on
+times rope_apply at an NTK-aware scaled base; `masked_prefill` times
+attn_prefill_masked (causal plus a key-padding mask) on LLaMA-7B-shaped heads.  `cpu_baseline` times the float64 oracle on a bounded sample on
 the host cores.
 
     python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
@@ -136,6 +137,26 @@ def _next_rows(R, dev, stream):
                      "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
                                   "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
         del q, kc, vc, o
+    # general additive mask: key padding (sequence 1 keeps 3000 of its 4096 keys) on top of the causal mask
+    Sm, lens_m = 4096, (4096, 3000)
+    q = torch.randn((B, Sm, H, D), generator=g, device=dev).to(torch.bfloat16)
+    k = torch.randn((B, Sm, H, D), generator=g, device=dev).to(torch.bfloat16)
+    v = torch.randn((B, Sm, H, D), generator=g, device=dev).to(torch.bfloat16)
+    mask = torch.zeros((B, 1, Sm, Sm), dtype=torch.bfloat16, device=dev)
+    for b, L in enumerate(lens_m):
+        mask[b, :, :, L:] = float("-inf")
+    o = torch.empty_like(q)
+    ms = _time_launches(lambda: R.attn_prefill_masked(q, k, v, mask, o, causal=True, scale=D ** -0.5), stream)
+    i = np.arange(Sm)
+    flops = 4.0 * D * H * float(sum(np.minimum(i + 1, L).sum() for L in lens_m))
+    tf = flops / (ms * 1e-3) / 1e12
+    out["masked_prefill"] = {"workload": f"B={B} S={Sm} Hq=Hkv={H} D={D} bf16 causal + key-padding mask "
+                                         f"[B,1,S,S] (keys kept {lens_m})",
+                             "value": round(tf, 2), "unit": "TFLOP/s", "launch_ms": round(ms, 4),
+                             "algorithmic_flops": flops,
+                             "roofline": {"bound": "mfma", "achieved": round(tf, 2), "peak": PEAK_BF16_TFLOPS,
+                                          "unit": "TFLOP/s", "frac": round(tf / PEAK_BF16_TFLOPS, 4)}}
+    del q, k, v, o, mask
     from rope_causal_gqa_amd import workloads as W
     gqa = {}
     for name in ("c4a", "c4b"):
@@ -351,6 +372,7 @@ def main():
         "chunked_prefill": extras.get("chunked_prefill"),
         "sliding_window": extras.get("sliding_window"),
         "gqa_prefill": extras.get("gqa_prefill"),
+        "masked_prefill": extras.get("masked_prefill"),
         "fused_rope_prefill": fused.get("fused_rope_prefill"),
         "fused_rope_decode": fused.get("fused_rope_decode"),
         "ntk_rope": fused.get("ntk_rope"),

@@ -156,6 +156,31 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
                           rcgqa_dtype dt, rcgqa_stream stream);
 
 /*
+ * attn_prefill_masked -- attn_prefill with a general additive mask.
+ *
+ * Defines: [HF] section 1.2 step 3 (the attention mask is sliced to the query
+ * and key lengths and added to the scaled scores before the fp32 softmax) and
+ * section 2 steps 4-5, for any mask: padding, per-head biases, custom
+ * patterns.  The causal mask can be applied on top.
+ *
+ *   out[b,i,h,:] = sum_j softmax_j(scale * q[b,i,h,:].k[b,j,h/G,:] + mask[b,h',i,j]
+ *                                  + (causal && j > i ? -inf : 0)) v[b,j,h/G,:]
+ *   h' = 0 when mask_heads == 1 (one mask shared by all query heads), else h.
+ *
+ * q, k, v, out  as attn_prefill ([B,S,Hq|Hkv,head_dim], head_dim 64 or 128).
+ * mask  [B, mask_heads, S, mask_ld] of the run's element type, row stride
+ *       mask_ld >= S elements (entries j >= S of a row are not read), 16-byte
+ *       aligned base; mask_heads is 1 or Hq.  -inf entries give zero weight; a
+ *       row with no finite score returns zeros.  Entries are added in fp32 to
+ *       the fp32 scores (bf16 masks are read exactly).
+ * out must not alias q, k, v or mask.
+ */
+rcgqa_status attn_prefill_masked(const void* q, const void* k, const void* v, const void* mask, void* out,
+                                 int B, int S, int Hq, int Hkv, int head_dim,
+                                 int mask_heads, int mask_ld, int causal, float scale,
+                                 rcgqa_dtype dt, rcgqa_stream stream);
+
+/*
  * attn_prefill_cache -- chunked / variable-length prefill against a KV cache,
  * with an optional causal sliding window.
  *

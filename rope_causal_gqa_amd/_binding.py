@@ -42,6 +42,8 @@ def lib():
     L.rope_apply_interleaved.restype = i32
     L.attn_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_prefill.restype = i32
+    L.attn_prefill_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.attn_prefill_masked.restype = i32
     L.attn_prefill_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_prefill_cache.restype = i32
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
@@ -169,6 +171,30 @@ def attn_prefill(q, k, v, out=None, causal=True, scale=None):
                             _dev(out, "out", dt, 4), B, S, Hq, Hkv, D, int(bool(causal)),
                             float(scale), dt, _stream(q))
     _check(st, "attn_prefill")
+    return out
+
+
+def attn_prefill_masked(q, k, v, mask, out=None, causal=False, scale=None):
+    """attn_prefill plus an additive mask [B, 1 or Hq, S, L >= S] of the run dtype (see rcgqa.h)."""
+    import torch
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    if mask.dim() != 4 or mask.shape[0] != B or mask.shape[1] not in (1, Hq) or mask.shape[2] != S \
+            or mask.shape[3] < S:
+        raise ValueError("mask must be [B, 1 or Hq, S, L] with L >= S")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B, S, Hq, D]")
+    scale = D ** -0.5 if scale is None else scale
+    st = lib().attn_prefill_masked(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), _dev(v, "v", dt, 4),
+                                   _dev(mask, "mask", dt, 4), _dev(out, "out", dt, 4), B, S, Hq, Hkv, D,
+                                   int(mask.shape[1]), int(mask.shape[3]), int(bool(causal)), float(scale), dt,
+                                   _stream(q))
+    _check(st, "attn_prefill_masked")
     return out
 
 

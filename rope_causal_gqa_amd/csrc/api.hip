@@ -129,6 +129,28 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
                                               Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
 }
 
+rcgqa_status attn_prefill_masked(const void* q, const void* k, const void* v, const void* mask, void* out, int B,
+                                 int S, int Hq, int Hkv, int head_dim, int mask_heads, int mask_ld, int causal,
+                                 float scale, rcgqa_dtype dt, rcgqa_stream stream) {
+  if (!q || !k || !v || !mask || !out || !good_dtype(dt) || !al16({q, k, v, mask, out})) return RCGQA_EINVAL;
+  if (out == q || out == k || out == v || out == mask) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
+  if ((mask_heads != 1 && mask_heads != Hq) || mask_ld < S) return RCGQA_EINVAL;
+  if (mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0 || mul({B, mask_heads, S, mask_ld}) < 0)
+    return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || (S + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  const hipStream_t st = (hipStream_t)stream;
+  const long long plane = (long long)S * mask_ld;
+  const rcgqa::KvSpec kv{(long long)S * Hkv * head_dim, head_dim, (long long)Hkv * head_dim, nullptr, S, 0,
+                         mask, (long long)mask_heads * plane, mask_heads == 1 ? 0 : plane, mask_ld};
+  if (dt == RCGQA_BF16)
+    return hip_status(
+        rcgqa::launch_prefill_bf16(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
+  return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, B, S,
+                                              Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
+}
+
 rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_lens,
                                 void* out, int B, int Sq, int Hq, int Hkv, int head_dim, int max_kv, int causal,
                                 int window, float scale, rcgqa_dtype dt, rcgqa_stream stream) {

@@ -13,11 +13,17 @@ namespace rcgqa {
 // count, clamped to [0, max_kv]; null means Sk = Sq.  Query i of a sequence
 // with Sk keys sits at absolute position i + Sk - Sq; with a causal mask it
 // sees keys j <= that position and, when window > 0, only j > position - window.
+//
+// mask (plain layout only; null = none): an additive mask of the run's element
+// type, entry (b, h, i, j) at mask[b*msb + h*msh + i*msr + j], added to the
+// scaled scores of query i and key j (msh = 0: shared by all query heads).
 struct KvSpec {
   long long sb, sh, sr;
   const int32_t* lens;
   int max_kv;
   int window;
+  const void* mask;
+  long long msb, msh, msr;
 };
 
 // q may be null with Hq == 0 (keys only).  table, when not null, receives each

@@ -98,7 +98,9 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
 // flight for grids too small to fill the GPU, with no memory outside the
 // workgroup).  BNT keys per K/V tile: 64, or 32 so that four groups' double
 // buffers fit in LDS.
-template <int D, int NW, bool GEN, int KSPLIT, int BNT>
+// MSK: an additive mask (kv.mask, plain layout) is added to the scores; each
+// lane loads its row's values for the next tile while the current one runs.
+template <int D, int NW, bool GEN, int KSPLIT, int BNT, bool MSK>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
                                                              int Sq, int Hq, int Hkv, int causal, float c_log2,
@@ -176,6 +178,37 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       rs[ks][1] = *reinterpret_cast<const f32x4*>(cs + D / 2 + i0 + 4);
     }
   }
+
+  // Additive mask: this lane's 2 NKB runs of 4 consecutive keys per tile (the
+  // score layout), one register set per tile buffer.  Rows past Sq read
+  // nothing; keys past the sequence read zeros (they are masked anyway).
+  bf16x4 mk[MSK ? 2 : 1][NKB][4];
+  const bf16* mrow = nullptr;
+  if constexpr (MSK) {
+    if (qrow < Sq)
+      mrow = reinterpret_cast<const bf16*>(kv.mask) + (size_t)b * kv.msb + (size_t)h * kv.msh + (size_t)qrow * kv.msr;
+  }
+  const bool mvec = (kv.msr & 3) == 0;  // 8-byte aligned runs (the base is 16-byte aligned)
+  auto load_mask = [&](int t, int set) __attribute__((always_inline)) {
+#pragma unroll
+    for (int kb2 = 0; kb2 < NKB; kb2++)
+#pragma unroll
+      for (int g4 = 0; g4 < 4; g4++) {
+        const int key = t * BN + kb2 * 32 + 8 * g4 + 4 * hf;
+        bf16x4 m4 = {};
+        if (mrow) {
+          if (mvec && key + 4 <= nkeys) {
+            m4 = *reinterpret_cast<const bf16x4*>(mrow + key);
+          } else {
+#pragma unroll
+            for (int c = 0; c < 4; c++)
+              if (key + c < nkeys) m4[c] = mrow[key + c];
+          }
+        }
+        mk[set][kb2][g4] = m4;
+      }
+  };
+  const float inv_scale = 1.4426950408889634f / c_log2;  // scores are kept unscaled
 
   // Tile loader: wave wr of a group fills tile rows [wr BN/NWG, (wr+1) BN/NWG) of K and V with
   // direct global->LDS loads.  Lane p of a load lands at physical chunk
@@ -261,6 +294,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     constexpr int buf = decltype(bufc)::value;
     const int kv0 = t * BN;
     if (t + 1 < tg_hi) issue(t + 1, buf ^ 1);
+    if constexpr (MSK) {
+      if (t + 1 < tg_hi) load_mask(t + 1, buf ^ 1);
+    }
     // else the whole tile is masked for this wave (past its last row, or before its window),
     // or (second key group, odd tile count) past the group's range
     if (t < tg_hi && !(causal && kv0 > wrow_hi + off) && !(W > 0 && kv0 + BN - 1 <= wrow_lo + off - W)) {
@@ -299,6 +335,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         vpre[db] = cat8(lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(sv) + voff[db][0])),
                         lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(sv) + voff[db][1])));
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (MSK) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; kb2++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) s[kb2][i] = fmaf((float)mk[buf][kb2][i >> 2][i & 3], inv_scale, s[kb2][i]);
+      }
       // mask (diagonal / tail tiles only) and row max on raw scores
       if ((causal && kv0 + BN - 1 > wrow_lo + off) || kv0 + BN > nkeys || (W > 0 && kv0 <= wrow_hi + off - W)) {
 #pragma unroll
@@ -365,6 +407,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     __syncthreads();                // ... and everyone's; tile t fully consumed
   };
   if (tg_lo < tg_hi) issue(tg_lo, 0);
+  if constexpr (MSK) {
+    if (tg_lo < tg_hi) load_mask(tg_lo, 0);
+  }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
   if (rot) {
@@ -450,14 +495,20 @@ static void launch_nw(const void* q, const void* k, const void* v, void* out, in
   constexpr int BM = 32 * NW / KSPLIT;
   const int nqt = (Sq + BM - 1) / BM;
   const dim3 grid((unsigned)((long long)B * Hq * npairs)), block(64 * NW);
-  if (D == 64)
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, NW, GEN, KSPLIT, BNT>), grid, block, 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv,
-                       q_rope);
-  else
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, NW, GEN, KSPLIT, BNT>), grid, block, 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv,
-                       q_rope);
+  // masks come with the plain layout only, so GEN kernels have no masked form
+  const bool msk = !GEN && kv.mask;
+#define RCGQA_PREFILL_LAUNCH(DD, M)                                                                               \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, NW, GEN, KSPLIT, BNT, M>), grid, block, 0, st, (const bf16*)q,    \
+                     (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv, \
+                     q_rope)
+  if (D == 64) {
+    if (msk) RCGQA_PREFILL_LAUNCH(64, !GEN);
+    else RCGQA_PREFILL_LAUNCH(64, false);
+  } else {
+    if (msk) RCGQA_PREFILL_LAUNCH(128, !GEN);
+    else RCGQA_PREFILL_LAUNCH(128, false);
+  }
+#undef RCGQA_PREFILL_LAUNCH
 }
 
 template <int NW, int KSPLIT, int BNT = 64>

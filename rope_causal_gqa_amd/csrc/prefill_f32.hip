@@ -10,7 +10,8 @@
 // in LDS and read as wave-wide broadcasts.  Causal tiles past the block's last
 // row (and, with a sliding window, before its first window) are never loaded.
 // Keys come through strides and per-sequence counts, so the same kernel serves
-// chunked / variable-length prefill against a cache.  Given a per-token
+// chunked / variable-length prefill against a cache; an optional additive
+// mask (plain layout) is added to each scaled score.  Given a per-token
 // cos/sin table, each lane first rotates its query row (RoPE fused into the
 // load, same arithmetic as the RoPE kernel).  This path targets accuracy
 // (1e-5 against fp64), not throughput.
@@ -54,6 +55,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const float* __restrict
       qr[D / 2 + d] = fmaf(bb, co, a * si);
     }
   }
+  const float* mrow = kv.mask && live ? reinterpret_cast<const float*>(kv.mask) + (size_t)b * kv.msb +
+                                            (size_t)h * kv.msh + (size_t)i * kv.msr
+                                      : nullptr;
   float m = -INFINITY, l = 0.f;
   // keys any row of this block can see: [key_lo, key_hi)
   const int key_hi = causal ? min(nk, q0 + BM + off) : nk;
@@ -82,7 +86,11 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const float* __restrict
       float dot = 0.f;
 #pragma unroll
       for (int d = 0; d < D; d++) dot = fmaf(qr[d], kr[d], dot);
-      const float s = dot * scale;
+      float s = dot * scale;
+      if (mrow) {
+        s += mrow[key];
+        if (!(s > -INFINITY)) continue;  // a masked key: no weight (and no -inf - -inf)
+      }
       if (s > m) {
         const float corr = expf(m - s);
         l *= corr;

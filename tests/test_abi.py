@@ -150,6 +150,7 @@ WS = ctypes.c_void_p(4096 * 64)
     lambda L: L.rope_apply(A[0], A[1], MIS, 1, 4, 8, 2, 64, 1e4, 1.0, 0, None),
     lambda L: L.attn_prefill(A[0], A[1], MIS, A[3], 1, 4, 8, 2, 64, 1, 0.125, 0, None),
     lambda L: L.attn_prefill_cache(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 16, 1, 0, 0.125, 0, None),
+    lambda L: L.attn_prefill_masked(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 1, 4, 1, 0.125, 0, None),
     lambda L: L.attn_decode(A[0], MIS, A[2], A[3], A[4], 1, 8, 2, 128, 16, 0.1, 0, WS, 1 << 30, None),
     lambda L: L.rope_attn_prefill(A[0], A[1], A[2], MIS, None, 1, 16, 8, 2, 64, 1, 0.125, 1e4, 1.0, 0, WS, 1 << 20,
                                   None),
@@ -267,3 +268,21 @@ def test_ntk_theta_rejects(args):
 def test_dynamic_ntk_theta_rejects(args):
     out = ctypes.c_float()
     assert R.lib().rope_dynamic_ntk_theta(*args, ctypes.byref(out)) == BD.EINVAL
+
+
+@pytest.mark.parametrize("args", [
+    dict(mask=None), dict(mask_heads=2), dict(mask_ld=3), dict(out_is_mask=True), dict(Hq=6, Hkv=4),
+    dict(causal=2), dict(scale=0.0), dict(D=7), dict(dt=4),
+])
+def test_prefill_masked_rejects(args):
+    a = dict(mask=A[3], B=1, S=4, Hq=8, Hkv=2, D=64, mask_heads=1, mask_ld=4, causal=1, scale=0.125, dt=0)
+    a.update(args)
+    out = a["mask"] if args.get("out_is_mask") else A[4]
+    st = R.lib().attn_prefill_masked(A[0], A[1], A[2], a["mask"], out, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"],
+                                     a["mask_heads"], a["mask_ld"], a["causal"], a["scale"], a["dt"], None)
+    assert st == BD.EINVAL
+
+
+def test_prefill_masked_unsupported_head_dim():
+    assert R.lib().attn_prefill_masked(A[0], A[1], A[2], A[3], A[4], 1, 4, 8, 2, 96, 8, 4, 1, 0.1, 0, None) \
+        == BD.EUNSUPPORTED

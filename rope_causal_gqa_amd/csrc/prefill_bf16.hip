@@ -119,7 +119,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   constexpr int ROWS_PER_LD = 64 / CH;      // rows one wave-wide 16-byte load fills
   constexpr int LD_PER_WAVE = BN / NWG / ROWS_PER_LD;
   static_assert(LD_PER_WAVE >= 1, "tile rows per wave");
-  __shared__ __attribute__((aligned(16))) bf16 lds[KSPLIT * 2 * 2 * TILE];  // [group][buffer][K | V][BN][D]
+  // With a mask on the 8-wave unsplit grid, mask tiles [BM rows][BN keys] are
+  // double-buffered in LDS after the K/V buffers.
+  constexpr bool MSTAGE = MSK && NW == 8 && KSPLIT == 1;
+  constexpr int MTILE = MSTAGE ? 32 * NW * BN : 0;
+  __shared__ __attribute__((aligned(16))) bf16 lds[KSPLIT * 2 * 2 * TILE + 2 * MTILE];  // [group][buffer][K | V][BN][D]
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -180,8 +184,30 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   }
 
   // Additive mask: this lane's 2 NKB runs of 4 consecutive keys per tile (the
-  // score layout), one register set per tile buffer.  Rows past Sq read
-  // nothing; keys past the sequence read zeros (they are masked anyway).
+  // score layout).  On the 8-wave unsplit grid (which the launcher uses for
+  // masks only when their rows hold a multiple of 8 entries) each tile's
+  // [BM][BN] block comes into LDS with the K/V tiles by direct loads (16-byte
+  // chunks; chunk c of block row r sits at chunk c ^ ((r >> 1) & 7), which
+  // spreads a wave's per-row reads over the banks).  The other grids read
+  // each lane's row from memory one tile ahead, into one register set per
+  // tile buffer; rows past Sq read nothing and keys past the sequence read
+  // zeros (they are masked anyway).
+  constexpr bool mstage = MSTAGE;
+  bf16* const mlds = lds + KSPLIT * 2 * 2 * TILE;
+  auto issue_mask = [&](int t, int buf) __attribute__((always_inline)) {
+    if constexpr (MSTAGE) {
+      constexpr int LDM = BM * BN * (int)sizeof(bf16) / 1024 / NW;  // 1 KB direct loads per wave
+      const bf16* mb = reinterpret_cast<const bf16*>(kv.mask) + (size_t)b * kv.msb + (size_t)h * kv.msh;
+#pragma unroll
+      for (int i = 0; i < LDM; i++) {
+        const int r0 = (wr * LDM + i) * 8;  // 8 block rows of BN keys per load
+        const int r = r0 + lane / 8, c = (lane % 8) ^ ((r >> 1) & 7);
+        const int row = min(q0 + r, Sq - 1);
+        const int key = min(t * BN + c * 8, (int)kv.msr - 8);  // inside the row; keys past Sq are masked
+        lds_dma16(mb + (size_t)row * kv.msr + key, mlds + buf * MTILE + r0 * BN);
+      }
+    }
+  };
   bf16x4 mk[MSK ? 2 : 1][NKB][4];
   const bf16* mrow = nullptr;
   if constexpr (MSK) {
@@ -190,6 +216,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   }
   const bool mvec = (kv.msr & 3) == 0;  // 8-byte aligned runs (the base is 16-byte aligned)
   auto load_mask = [&](int t, int set) __attribute__((always_inline)) {
+    if constexpr (mstage) return;
 #pragma unroll
     for (int kb2 = 0; kb2 < NKB; kb2++)
 #pragma unroll
@@ -295,7 +322,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     const int kv0 = t * BN;
     if (t + 1 < tg_hi) issue(t + 1, buf ^ 1);
     if constexpr (MSK) {
-      if (t + 1 < tg_hi) load_mask(t + 1, buf ^ 1);
+      if (t + 1 < tg_hi) {
+        if (mstage) issue_mask(t + 1, buf ^ 1);
+        load_mask(t + 1, buf ^ 1);
+      }
     }
     // else the whole tile is masked for this wave (past its last row, or before its window),
     // or (second key group, odd tile count) past the group's range
@@ -336,6 +366,15 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
                         lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(sv) + voff[db][1])));
       __builtin_amdgcn_sched_barrier(0);
       if constexpr (MSK) {
+        if (mstage) {
+          const int rr = wr * 32 + col;  // this lane's row of the block
+          const bf16* mt = mlds + buf * MTILE + rr * BN + 4 * hf;
+#pragma unroll
+          for (int kb2 = 0; kb2 < NKB; kb2++)
+#pragma unroll
+            for (int g4 = 0; g4 < 4; g4++)
+              mk[buf][kb2][g4] = *reinterpret_cast<const bf16x4*>(mt + (((kb2 * 4 + g4) ^ ((rr >> 1) & 7)) * 8));
+        }
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; kb2++)
 #pragma unroll
@@ -408,7 +447,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   };
   if (tg_lo < tg_hi) issue(tg_lo, 0);
   if constexpr (MSK) {
-    if (tg_lo < tg_hi) load_mask(tg_lo, 0);
+    if (tg_lo < tg_hi) {
+      if (mstage) issue_mask(tg_lo, 0);
+      load_mask(tg_lo, 0);
+    }
   }
   __builtin_amdgcn_s_waitcnt(0);
   __syncthreads();
@@ -557,7 +599,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   // take 128-row tiles (window 256: 104 -> 86 us, 1024: 170 -> 164 us on
   // B=2 S=4096 Hq=Hkv=32 D=128).
   const bool short_window = kv.window > 0 && kv.window < 2048;
-  if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512 && !short_window) {
+  // the 8-wave grid stages mask tiles in LDS with 16-byte loads: rows of a multiple of 8 entries
+  const bool mask_ok = !kv.mask || (kv.msr % 8 == 0 && kv.msr >= 8);
+  if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512 && !short_window && mask_ok) {
     launch_nw<8, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, kv, q_rope, st);
   } else {
     const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;

@@ -62,6 +62,9 @@ CASES = [
     (2, 70, 4, 2, 64, True, "fp32", "pad", 70),
     (1, 97, 4, 2, 128, False, "fp32", "alibi", 99),
     (2, 200, 4, 2, 128, False, "bf16", "dead_rows", 200),
+    (2, 2048, 32, 8, 128, True, "bf16", "pad", 2048),      # 8-wave grid, mask tiles staged in LDS
+    (2, 2048, 32, 8, 128, True, "bf16", "alibi", 2056),    # same, per-head mask, padded rows
+    (2, 2048, 32, 8, 64, True, "bf16", "pad_left", 2052),  # rows not a multiple of 8: another grid
     (1, 2100, 8, 1, 128, True, "bf16", "pad", 2100),       # four key groups
     (1, 2100, 16, 2, 64, True, "bf16", "alibi", 2104),     # two key groups
 ]

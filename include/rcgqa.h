@@ -16,7 +16,9 @@
  *
  * Conventions shared by every entry point:
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
- *     allocates nothing, frees nothing and keeps no mutable global state.
+ *     allocates nothing and frees nothing.  Its only mutable state is a
+ *     per-thread memo of the last prefill grid choice (a pure function of the
+ *     shape), so calls from several threads are safe.
  *   - Tensors are dense and row-major with head_dim innermost.  Element type is
  *     selected by `dt`: RCGQA_BF16 (bfloat16 storage, fp32 arithmetic) or
  *     RCGQA_FP32.  Tensor pointers must be 16-byte aligned (the kernels move

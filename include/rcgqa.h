@@ -33,6 +33,11 @@
  *     read on the host; the kernels clamp them as documented per call.
  *   - Sizes are int; the element count of every tensor must fit in int64 and
  *     B*S (and B*Hq) must fit in int32.
+ *   - Grid limits (RCGQA_EUNSUPPORTED): the prefill entry points take at most
+ *     4194240 query rows per sequence and B*Hq*ceil(S/128) <= 2^24 - 1 (about
+ *     2^31 query rows in all, more than q and out could fill in one GPU's
+ *     memory); the decode entry points and kv_append at most 65535 sequences
+ *     and 65535 heads.
  */
 #ifndef RCGQA_H
 #define RCGQA_H

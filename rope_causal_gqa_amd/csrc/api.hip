@@ -37,6 +37,18 @@ int64_t mul(std::initializer_list<int64_t> xs) {
 
 bool attn_head_dim(int d) { return d == 64 || d == 128; }
 
+// Grid limits of the prefill kernels.  Query rows of a sequence are tiled in
+// at most 65535 blocks of 64 in the fp32 kernel's second grid dimension, and
+// no prefill grid launches more than two work-items per query row once each
+// (batch, head)'s rows are padded to a multiple of 128; a dispatch counts its
+// work-items in 32 bits.  (2^32 work-items means about 2^31 query rows: q and
+// out alone would not fit in one GPU's memory.)
+bool prefill_grid_ok(int B, int Hq, int S) {
+  if ((S + 63) / 64 > 65535) return false;
+  const int64_t items = mul({B, Hq, (S + 127) / 128, 256});
+  return items > 0 && items <= (int64_t)UINT32_MAX;
+}
+
 rcgqa_status hip_status(hipError_t e) { return e == hipSuccess ? RCGQA_OK : RCGQA_EHIP; }
 
 // Host checks shared by the two pairings of the rotation.
@@ -118,7 +130,7 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
   if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
   if (mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0) return RCGQA_EINVAL;
-  if (!attn_head_dim(head_dim) || (S + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  if (!attn_head_dim(head_dim) || !prefill_grid_ok(B, Hq, S)) return RCGQA_EUNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
   // K/V in [B, S, Hkv, D]: every sequence has S keys, queries aligned with them
   const rcgqa::KvSpec kv{(long long)S * Hkv * head_dim, head_dim, (long long)Hkv * head_dim, nullptr, S, 0};
@@ -139,7 +151,7 @@ rcgqa_status attn_prefill_masked(const void* q, const void* k, const void* v, co
   if ((mask_heads != 1 && mask_heads != Hq) || mask_ld < S) return RCGQA_EINVAL;
   if (mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0 || mul({B, mask_heads, S, mask_ld}) < 0)
     return RCGQA_EINVAL;
-  if (!attn_head_dim(head_dim) || (S + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  if (!attn_head_dim(head_dim) || !prefill_grid_ok(B, Hq, S)) return RCGQA_EUNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
   const long long plane = (long long)S * mask_ld;
   const rcgqa::KvSpec kv{(long long)S * Hkv * head_dim, head_dim, (long long)Hkv * head_dim, nullptr, S, 0,
@@ -163,7 +175,7 @@ rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* 
   if (window < 0 || (window > 0 && causal == 0)) return RCGQA_EINVAL;
   if (mul({B, Hq}) > kI32Max || mul({B, Sq, Hq, head_dim}) < 0 || mul({B, Hkv, max_kv, head_dim}) < 0)
     return RCGQA_EINVAL;
-  if (!attn_head_dim(head_dim) || (Sq + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  if (!attn_head_dim(head_dim) || !prefill_grid_ok(B, Hq, Sq)) return RCGQA_EUNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
   // caches [B, Hkv, max_kv, D]: rows of one (batch, KV head) are contiguous
   const rcgqa::KvSpec kv{(long long)Hkv * max_kv * head_dim, (long long)max_kv * head_dim, head_dim, kv_lens,
@@ -194,7 +206,7 @@ rcgqa_status rope_attn_prefill(const void* q, void* k, const void* v, void* out,
   const int64_t tokens = mul({B, S});
   if (tokens < 0 || tokens > kI32Max || mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0) return RCGQA_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return RCGQA_EINVAL;
-  if (!attn_head_dim(head_dim) || (S + 63) / 64 > 65535) return RCGQA_EUNSUPPORTED;
+  if (!attn_head_dim(head_dim) || !prefill_grid_ok(B, Hq, S)) return RCGQA_EUNSUPPORTED;
   if (workspace_bytes < rope_attn_prefill_workspace_bytes(B, S, head_dim)) return RCGQA_EINVAL;
   const hipStream_t st = (hipStream_t)stream;
   float* table = (float*)workspace;
@@ -222,9 +234,9 @@ rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache
   if (!al16({q, k_cache, v_cache, out}) || !al4(kv_lens)) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
-  if (B > 65535 || Hq > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
+  if (mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return RCGQA_EINVAL;
-  if (!attn_head_dim(head_dim) || Hq / Hkv > 16) return RCGQA_EUNSUPPORTED;
+  if (!attn_head_dim(head_dim) || Hq / Hkv > 16 || B > 65535 || Hq > 65535) return RCGQA_EUNSUPPORTED;
   if (workspace_bytes < rcgqa::decode_workspace_bytes(B, Hq, head_dim, max_kv)) return RCGQA_EINVAL;
   return hip_status(rcgqa::launch_decode(q, k_cache, v_cache, kv_lens, out, B, Hq, Hkv, head_dim, max_kv, scale,
                                          dt == RCGQA_BF16, workspace, (hipStream_t)stream));
@@ -247,10 +259,9 @@ rcgqa_status rope_attn_decode(const void* q, const void* k_new, const void* v_ne
   if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
   if (!finite_pos(theta) || !finite_pos(linear_factor)) return RCGQA_EINVAL;
-  if (B > 65535 || Hq > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0 || mul({B, Hq, head_dim, 4}) < 0)
-    return RCGQA_EINVAL;
+  if (mul({B, Hkv, max_kv, head_dim}) < 0 || mul({B, Hq, head_dim, 4}) < 0) return RCGQA_EINVAL;
   if (reinterpret_cast<uintptr_t>(workspace) % 256) return RCGQA_EINVAL;
-  if (!attn_head_dim(head_dim) || Hq / Hkv > 16) return RCGQA_EUNSUPPORTED;
+  if (!attn_head_dim(head_dim) || Hq / Hkv > 16 || B > 65535 || Hq > 65535) return RCGQA_EUNSUPPORTED;
   if (workspace_bytes < rope_attn_decode_workspace_bytes(B, Hq, head_dim, max_kv)) return RCGQA_EINVAL;
   const hipStream_t st = (hipStream_t)stream;
   // rotated queries first (256-byte aligned), the split-K partial states after them
@@ -270,8 +281,8 @@ rcgqa_status kv_append(void* k_cache, void* v_cache, const void* k_new, const vo
   if (!k_cache || !v_cache || !k_new || !v_new || !slots || !good_dtype(dt)) return RCGQA_EINVAL;
   if (!al16({k_cache, v_cache, k_new, v_new}) || !al4(slots)) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(Hkv) || !pos_int(max_kv) || head_dim < 2 || head_dim % 2) return RCGQA_EINVAL;
-  if (B > 65535 || Hkv > 65535 || mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
-  if (head_dim > 256) return RCGQA_EUNSUPPORTED;
+  if (mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
+  if (head_dim > 256 || B > 65535 || Hkv > 65535) return RCGQA_EUNSUPPORTED;
   return hip_status(rcgqa::launch_kv_append(k_cache, v_cache, k_new, v_new, slots, B, Hkv, head_dim, max_kv,
                                             dt == RCGQA_BF16, (hipStream_t)stream));
 }

@@ -5,7 +5,8 @@
 // section 6.1 (linear scaling divides positions by the factor).  Pairing is
 // (x[i], x[i + D/2]) with angle (pos / factor) * theta^(-2i/D).
 //
-// Design: one workgroup per token.  The token's D/2 angles are formed in fp64
+// Design: one workgroup per token (a workgroup takes several tokens, a grid
+// apart, only when there are more than kMaxTokenGroups).  The token's D/2 angles are formed in fp64
 // (exact enough for the fp32 path's 1e-5 bound at positions in the thousands)
 // and their cos/sin rounded to fp32 into LDS once; every head of q and k at
 // that token then reuses them.  Each thread moves 16-byte vectors of the two
@@ -25,6 +26,10 @@
 #include "launch.h"
 
 namespace rcgqa {
+
+// Largest grid of the per-token kernels: 2^20 workgroups of 256 work-items
+// keep the launch far inside the 32-bit work-item count of a dispatch.
+constexpr int kMaxTokenGroups = 1 << 20;
 
 template <typename T, int VE>
 struct alignas(sizeof(T) * VE) Vec {
@@ -65,23 +70,25 @@ __device__ __forceinline__ void rope_pair(const T* s1, const T* s2, T* d1, T* d2
 // token's cos/sin row: table[tok * D + i] = cos, table[tok * D + D/2 + i] = sin.
 template <typename T, int VE>
 __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restrict__ k,
-                                                   const int32_t* __restrict__ pos_ids, int S, int Hq,
-                                                   int Hkv, int D, double theta, double factor,
+                                                   const int32_t* __restrict__ pos_ids, long long ntok, int S,
+                                                   int Hq, int Hkv, int D, double theta, double factor,
                                                    float* __restrict__ table) {
   extern __shared__ float cs[];  // cos[D/2] then sin[D/2]
-  const int tok = blockIdx.x;
   const int half = D >> 1;
-  const int pos = pos_ids ? pos_ids[tok] : (tok % S);
-  rope_angles(cs, pos, D, theta, factor);
-  __syncthreads();
-  if (table)
-    for (int i = threadIdx.x; i < D; i += blockDim.x) table[(size_t)tok * D + i] = cs[i];
   const int cpr = half / VE;  // vectors per half head-vector
   const int units = (Hq + Hkv) * cpr;
-  for (int u = threadIdx.x; u < units; u += blockDim.x) {
-    const int head = u / cpr, c = u - head * cpr;
-    T* base = head < Hq ? q + ((size_t)tok * Hq + head) * D : k + ((size_t)tok * Hkv + (head - Hq)) * D;
-    rope_pair<T, VE>(base + c * VE, base + half + c * VE, base + c * VE, base + half + c * VE, cs, c, half);
+  for (long long tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
+    if (tok != (long long)blockIdx.x) __syncthreads();  // the previous token's cs fully read
+    const int pos = pos_ids ? pos_ids[tok] : (int)(tok % S);
+    rope_angles(cs, pos, D, theta, factor);
+    __syncthreads();
+    if (table)
+      for (int i = threadIdx.x; i < D; i += blockDim.x) table[(size_t)tok * D + i] = cs[i];
+    for (int u = threadIdx.x; u < units; u += blockDim.x) {
+      const int head = u / cpr, c = u - head * cpr;
+      T* base = head < Hq ? q + ((size_t)tok * Hq + head) * D : k + ((size_t)tok * Hkv + (head - Hq)) * D;
+      rope_pair<T, VE>(base + c * VE, base + half + c * VE, base + c * VE, base + half + c * VE, cs, c, half);
+    }
   }
 }
 
@@ -89,30 +96,33 @@ __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restr
 // head vector is (x[2i], x[2i+1]) with the angle of frequency index i.
 template <typename T, int VE>
 __global__ __launch_bounds__(256) void rope_interleaved_kernel(T* __restrict__ q, T* __restrict__ k,
-                                                               const int32_t* __restrict__ pos_ids, int S, int Hq,
-                                                               int Hkv, int D, double theta, double factor) {
+                                                               const int32_t* __restrict__ pos_ids,
+                                                               long long ntok, int S, int Hq, int Hkv, int D,
+                                                               double theta, double factor) {
   extern __shared__ float cs[];  // cos[D/2] then sin[D/2]
-  const int tok = blockIdx.x;
   const int half = D >> 1;
-  const int pos = pos_ids ? pos_ids[tok] : (tok % S);
-  rope_angles(cs, pos, D, theta, factor);
-  __syncthreads();
   const int cpr = D / VE;  // vectors per head vector
   const int units = (Hq + Hkv) * cpr;
-  for (int u = threadIdx.x; u < units; u += blockDim.x) {
-    const int head = u / cpr, c = u - head * cpr;
-    T* p = (head < Hq ? q + ((size_t)tok * Hq + head) * D : k + ((size_t)tok * Hkv + (head - Hq)) * D) + c * VE;
-    const Vec<T, VE> x = *reinterpret_cast<const Vec<T, VE>*>(p);
-    Vec<T, VE> y;
+  for (long long tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
+    if (tok != (long long)blockIdx.x) __syncthreads();  // the previous token's cs fully read
+    const int pos = pos_ids ? pos_ids[tok] : (int)(tok % S);
+    rope_angles(cs, pos, D, theta, factor);
+    __syncthreads();
+    for (int u = threadIdx.x; u < units; u += blockDim.x) {
+      const int head = u / cpr, c = u - head * cpr;
+      T* p = (head < Hq ? q + ((size_t)tok * Hq + head) * D : k + ((size_t)tok * Hkv + (head - Hq)) * D) + c * VE;
+      const Vec<T, VE> x = *reinterpret_cast<const Vec<T, VE>*>(p);
+      Vec<T, VE> y;
 #pragma unroll
-    for (int j = 0; j < VE / 2; j++) {
-      const int i = c * (VE / 2) + j;
-      const float co = cs[i], si = cs[half + i];
-      const float a = (float)x.v[2 * j], b = (float)x.v[2 * j + 1];
-      y.v[2 * j] = (T)fmaf(a, co, -(b * si));
-      y.v[2 * j + 1] = (T)fmaf(b, co, a * si);
+      for (int j = 0; j < VE / 2; j++) {
+        const int i = c * (VE / 2) + j;
+        const float co = cs[i], si = cs[half + i];
+        const float a = (float)x.v[2 * j], b = (float)x.v[2 * j + 1];
+        y.v[2 * j] = (T)fmaf(a, co, -(b * si));
+        y.v[2 * j + 1] = (T)fmaf(b, co, a * si);
+      }
+      *reinterpret_cast<Vec<T, VE>*>(p) = y;
     }
-    *reinterpret_cast<Vec<T, VE>*>(p) = y;
   }
 }
 
@@ -159,22 +169,23 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
 
 hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
                        double theta, double factor, bool bf16_io, float* table, hipStream_t st) {
-  const dim3 grid((unsigned)((long)B * S)), block(256);
+  const long long ntok = (long long)B * S;
+  const dim3 grid((unsigned)(ntok < kMaxTokenGroups ? ntok : kMaxTokenGroups)), block(256);
   const size_t lds = (size_t)D * sizeof(float);
   const int half = D / 2;
   if (bf16_io) {
     if (half % 8 == 0)
-      hipLaunchKernelGGL((rope_kernel<bf16, 8>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq, Hkv, D,
+      hipLaunchKernelGGL((rope_kernel<bf16, 8>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, ntok, S, Hq, Hkv, D,
                          theta, factor, table);
     else
-      hipLaunchKernelGGL((rope_kernel<bf16, 1>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq, Hkv, D,
+      hipLaunchKernelGGL((rope_kernel<bf16, 1>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, ntok, S, Hq, Hkv, D,
                          theta, factor, table);
   } else {
     if (half % 4 == 0)
-      hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, lds, st, (float*)q, (float*)k, pos, S, Hq, Hkv,
+      hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, lds, st, (float*)q, (float*)k, pos, ntok, S, Hq, Hkv,
                          D, theta, factor, table);
     else
-      hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, lds, st, (float*)q, (float*)k, pos, S, Hq, Hkv,
+      hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, lds, st, (float*)q, (float*)k, pos, ntok, S, Hq, Hkv,
                          D, theta, factor, table);
   }
   return hipGetLastError();
@@ -182,21 +193,22 @@ hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int H
 
 hipError_t launch_rope_interleaved(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
                                   double theta, double factor, bool bf16_io, hipStream_t st) {
-  const dim3 grid((unsigned)((long)B * S)), block(256);
+  const long long ntok = (long long)B * S;
+  const dim3 grid((unsigned)(ntok < kMaxTokenGroups ? ntok : kMaxTokenGroups)), block(256);
   const size_t lds = (size_t)D * sizeof(float);
   if (bf16_io) {
     if (D % 8 == 0)
-      hipLaunchKernelGGL((rope_interleaved_kernel<bf16, 8>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq,
+      hipLaunchKernelGGL((rope_interleaved_kernel<bf16, 8>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, ntok, S, Hq,
                          Hkv, D, theta, factor);
     else
-      hipLaunchKernelGGL((rope_interleaved_kernel<bf16, 2>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, S, Hq,
+      hipLaunchKernelGGL((rope_interleaved_kernel<bf16, 2>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, ntok, S, Hq,
                          Hkv, D, theta, factor);
   } else {
     if (D % 4 == 0)
-      hipLaunchKernelGGL((rope_interleaved_kernel<float, 4>), grid, block, lds, st, (float*)q, (float*)k, pos, S,
+      hipLaunchKernelGGL((rope_interleaved_kernel<float, 4>), grid, block, lds, st, (float*)q, (float*)k, pos, ntok, S,
                          Hq, Hkv, D, theta, factor);
     else
-      hipLaunchKernelGGL((rope_interleaved_kernel<float, 2>), grid, block, lds, st, (float*)q, (float*)k, pos, S,
+      hipLaunchKernelGGL((rope_interleaved_kernel<float, 2>), grid, block, lds, st, (float*)q, (float*)k, pos, ntok, S,
                          Hq, Hkv, D, theta, factor);
   }
   return hipGetLastError();

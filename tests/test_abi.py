@@ -132,6 +132,35 @@ def test_decode_unsupported_group():
     assert st == BD.EUNSUPPORTED
 
 
+@pytest.mark.parametrize("B,S,Hq,Hkv", [
+    (1, 65535 * 64 + 1, 8, 2),     # more than 65535 64-row blocks in one sequence
+    (1 << 16, 1, 512, 512),        # 2^25 (batch, head) pairs x 256 work-items > 2^32
+    (1 << 12, 2049, 256, 256),     # 2^20 pairs x 17 row blocks of 128 x 256 > 2^32
+])
+def test_prefill_grid_limits(B, S, Hq, Hkv):
+    L = R.lib()
+    O = ctypes.c_void_p(8192)
+    assert L.attn_prefill(FAKE, FAKE, FAKE, O, B, S, Hq, Hkv, 64, 1, 0.1, 0, None) == BD.EUNSUPPORTED
+    assert L.attn_prefill_masked(FAKE, FAKE, FAKE, FAKE, O, B, S, Hq, Hkv, 64, 1, S, 1, 0.1, 0, None) \
+        == BD.EUNSUPPORTED
+    assert L.attn_prefill_cache(FAKE, FAKE, FAKE, FAKE, O, B, S, Hq, Hkv, 64, S, 1, 0, 0.1, 0, None) \
+        == BD.EUNSUPPORTED
+    q, k, v = (ctypes.c_void_p(4096 * i) for i in (3, 4, 5))
+    assert L.rope_attn_prefill(q, k, v, O, None, B, S, Hq, Hkv, 64, 1, 0.1, 1e4, 1.0, 0, FAKE, 1 << 62,
+                               None) == BD.EUNSUPPORTED
+
+
+@pytest.mark.parametrize("B,Hq,Hkv", [(65536, 8, 2), (2, 65536 * 2, 65536)])
+def test_decode_grid_limits(B, Hq, Hkv):
+    L = R.lib()
+    ws = ctypes.c_void_p(4096 * 16)
+    assert L.attn_decode(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(8192), B, Hq, Hkv, 128, 16, 0.1, 0, ws, 1 << 62,
+                         None) == BD.EUNSUPPORTED
+    assert L.rope_attn_decode(FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, ctypes.c_void_p(8192), B, Hq, Hkv, 128, 16,
+                              0.1, 1e4, 1.0, 0, ws, 1 << 62, None) == BD.EUNSUPPORTED
+    assert L.kv_append(FAKE, FAKE, FAKE, FAKE, FAKE, B, min(Hkv, 65536), 64, 4, 0, None) == BD.EUNSUPPORTED
+
+
 def test_kv_append_rejects():
     L = R.lib()
     assert L.kv_append(FAKE, FAKE, FAKE, FAKE, None, 1, 1, 64, 4, 0, None) == BD.EINVAL

@@ -119,3 +119,27 @@ def test_rope_ntk_scaled_base(dtype):
     _run(q, k, pos, static, 1.0, dtype, f"rope NTK static scale 8 {dtype}")
     pos = rng.integers(0, 8192, size=(2, 48)).astype(np.int32)
     _run(q, k, pos, dynamic, 1.0, dtype, f"rope NTK dynamic 8192/4096 {dtype}")
+
+
+@pytest.mark.parametrize("style", ["half", "interleaved"])
+def test_rope_more_tokens_than_workgroups(style):
+    """2^20 + 74 tokens: the grid stops at 2^20 workgroups, so the last 74
+    tokens are a second token of the first 74 workgroups.  Checked on those
+    tokens, their neighbours and a sample of the rest, at default positions."""
+    import torch
+    B, S, Hq, Hkv, D = 2, (1 << 19) + 37, 2, 1, 8
+    announce(f"rope {style} {B * S} tokens (grid-stride)")
+    q = W.random_case(91, (B, S, Hq, D), "bf16")
+    k = W.random_case(92, (B, S, Hkv, D), "bf16")
+    qd, kd = dev(q, "bf16"), dev(k, "bf16")
+    (R.rope_apply if style == "half" else R.rope_apply_interleaved)(qd, kd, None, 1e4, 1.0)
+    torch.cuda.synchronize()
+    rng = np.random.Generator(np.random.PCG64(93))
+    tail = np.arange(S - 200, S)
+    for b, idx in ((0, np.sort(rng.choice(S, 300, replace=False))), (1, tail)):
+        pos = idx.reshape(1, -1).astype(np.int32)
+        qr, kr = oracle.rope_apply(W.to_f64(q[b:b + 1, idx], "bf16"), W.to_f64(k[b:b + 1, idx], "bf16"), pos,
+                                   1e4, 1.0, style=style)
+        ti = torch.from_numpy(idx).cuda()
+        check(host64(qd[b:b + 1, ti]), qr, "bf16", f"rope {style} sequence {b} sampled q")
+        check(host64(kd[b:b + 1, ti]), kr, "bf16", f"rope {style} sequence {b} sampled k")

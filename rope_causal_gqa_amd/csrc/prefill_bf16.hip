@@ -20,10 +20,12 @@
 //    output layout every lane then owns ONE query row (lane % 32) and 32 of
 //    the tile's 64 keys; the other 32 sit in lane ^ 32, so row max / row sum
 //    need one v_permlane32_swap and no LDS.
-//  * Online softmax in the exp2 domain with fp32 running max / sum per lane;
-//    the scale is folded into one FMA before the exp, and the reference max
-//    only moves when a row's max grows by more than 2^8 (lazy rescale), so
-//    the O rescale is skipped on almost every tile.
+//  * Online softmax in the exp2 domain with fp32 running max / sum per lane.
+//    The query registers carry scale * log2(e) (rounded to bf16), and each
+//    tile's Q K^T product starts from the accumulator value -m_ref, the row's
+//    reference max, so the weights are a bare exp2 of the product.  The
+//    reference only moves when a row's max grows by more than 2^8 (lazy
+//    rescale), so the O rescale is skipped on almost every tile.
 //  * O^T = V^T P^T, again 32x32x16: P^T comes straight from the score
 //    registers (converted to bf16; the MFMA's k index is permuted to match the
 //    score layout), V^T is read from the row-major V tile with the gfx950 LDS
@@ -235,7 +237,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         mk[set][kb2][g4] = m4;
       }
   };
-  const float inv_scale = 1.4426950408889634f / c_log2;  // scores are kept unscaled
+  constexpr float kLog2e = 1.4426950408889634f;  // the mask enters the log2-unit scores as mask * log2(e)
 
   // Tile loader: wave wr of a group fills tile rows [wr BN/NWG, (wr+1) BN/NWG) of K and V with
   // direct global->LDS loads.  Lane p of a load lands at physical chunk
@@ -279,11 +281,17 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   f32x16 o[DB];
 #pragma unroll
   for (int db = 0; db < DB; db++) o[db] = f32x16{};
-  // A finite start for the running max: a row whose first tiles are fully
-  // masked (sliding window) then keeps zero weights instead of exp2(-inf + inf).
-  // m_lim = m_run + the lazy-rescale margin; nmc = -m_run * c_log2 (the exp offset).
-  float m_run = -1e30f, l_run = 0.f;
-  float m_lim = m_run, nmc = -m_run * c_log2;
+  // Scores are formed in log2 units (the query registers carry scale * log2(e))
+  // and relative to the row's reference max m_ref: every tile's Q K^T product
+  // starts from the accumulator value -m_ref (negm), so the weights are plain
+  // exp2 of the scores.  `lim` is the lazy-rescale threshold on those relative
+  // scores; -1e30 marks a row that has not seen a visible key yet (m_ref = 0
+  // meanwhile), so a row whose first tiles are fully masked keeps zero weights.
+  // (The masked two-group kernel, whose per-lane mask registers leave no room
+  // for the 16 offset registers, subtracts m_ref after the product instead.)
+  constexpr bool NEGM = !(MSK && KSPLIT == 2);
+  float m_ref = 0.f, l_run = 0.f, lim = -1e30f;
+  f32x16 negm = {};
 
   // keys any row of this query tile can see: tiles [t_lo, t_hi)
   const int key_hi = causal ? min(nkeys, q0 + BM + off) : nkeys;
@@ -293,7 +301,6 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int ntl = max(t_hi - t_lo, 0), steps = (ntl + KSPLIT - 1) / KSPLIT;
   const int tg_lo = t_lo + grp * steps, tg_hi = min(tg_lo + steps, t_lo + ntl);
   const int wrow_lo = q0 + wr * 32, wrow_hi = wrow_lo + 31;
-  const float rescale_margin = kRescaleLog2 / c_log2;  // the lazy-rescale threshold in score units
 
   // transpose-read addressing of V (fixed per lane)
   const int r16 = lane & 15, g = lane >> 4;
@@ -333,17 +340,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       const bf16* sk = ldsg + buf * 2 * TILE;
       const bf16* sv = sk + TILE;
 
-      // S^T = K Q^T: NKB 32-key blocks, chains interleaved
+      // S^T = K Q^T - m_ref: NKB 32-key blocks, chains interleaved
       f32x16 s[NKB];
-#pragma unroll
-      for (int kb2 = 0; kb2 < NKB; kb2++) s[kb2] = f32x16{};
 #pragma unroll
       for (int ks = 0; ks < KS; ks++) {
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; kb2++) {
           const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(sk) + koff[ks] +
                                                             kb2 * 32 * D * (int)sizeof(bf16));
-          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], s[kb2], 0, 0, 0);
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks > 0 ? s[kb2] : NEGM ? negm : f32x16{}, 0,
+                                                           0, 0);
         }
       }
       if (PREF > 0) {
@@ -365,6 +371,10 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         vpre[db] = cat8(lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(sv) + voff[db][0])),
                         lds_read_tr16(reinterpret_cast<const bf16*>(reinterpret_cast<const char*>(sv) + voff[db][1])));
       __builtin_amdgcn_sched_barrier(0);
+      if constexpr (!NEGM) {
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; kb2++) s[kb2] -= m_ref;
+      }
       if constexpr (MSK) {
         if (mstage) {
           const int rr = wr * 32 + col;  // this lane's row of the block
@@ -378,9 +388,9 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; kb2++)
 #pragma unroll
-          for (int i = 0; i < 16; i++) s[kb2][i] = fmaf((float)mk[buf][kb2][i >> 2][i & 3], inv_scale, s[kb2][i]);
+          for (int i = 0; i < 16; i++) s[kb2][i] = fmaf((float)mk[buf][kb2][i >> 2][i & 3], kLog2e, s[kb2][i]);
       }
-      // mask (diagonal / tail tiles only) and row max on raw scores
+      // mask (diagonal / tail tiles only) and row max
       if ((causal && kv0 + BN - 1 > wrow_lo + off) || kv0 + BN > nkeys || (W > 0 && kv0 <= wrow_hi + off - W)) {
 #pragma unroll
         for (int kb2 = 0; kb2 < NKB; kb2++)
@@ -399,23 +409,32 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         for (int i = 0; i < 16; i++) mx = fmaxf(mx, s[kb2][i]);
       mx = half_swap_max(mx);
 
-      // lazy rescale: move the reference max only when some row grew by more
-      // than 2^kRescaleLog2 (exact either way: O and l share the reference)
-      if (__any(mx > m_lim)) {
-        const float m_new = fmaxf(m_run, mx);
-        const float alpha = fast_exp2((m_run - m_new) * c_log2);
+      // lazy rescale: move the reference only in rows whose max grew by more
+      // than 2^kRescaleLog2 (exact either way: O and l share the reference),
+      // or that see their first visible key
+      if (__any(mx > lim)) {
+        const bool up = mx > lim;
+        const float d = up ? mx : 0.f;
+        const float alpha = up && lim > -1e29f ? fast_exp2(-mx) : 1.f;  // O = l = 0 before the first key
         l_run *= alpha;
 #pragma unroll
         for (int db = 0; db < DB; db++) o[db] *= alpha;
-        m_run = m_new;
-        m_lim = m_new + rescale_margin;
-        nmc = -m_new * c_log2;
+        m_ref += d;
+        lim = up ? kRescaleLog2 : lim;
+        if constexpr (NEGM) {
+#pragma unroll
+          for (int i = 0; i < 16; i++) negm[i] = -m_ref;
+        }
+#pragma unroll
+        for (int kb2 = 0; kb2 < NKB; kb2++)
+#pragma unroll
+          for (int i = 0; i < 16; i++) s[kb2][i] -= d;
       }
       bf16x8 pf[2 * NKB];
 #pragma unroll
       for (int kb2 = 0; kb2 < NKB; kb2++) {
 #pragma unroll
-        for (int i = 0; i < 16; i++) pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)fast_exp2(fmaf(s[kb2][i], c_log2, nmc));
+        for (int i = 0; i < 16; i++) pf[kb2 * 2 + (i >> 3)][i & 7] = (bf16)fast_exp2(s[kb2][i]);
       }
       // row sum of the bf16 weights actually fed to the MFMA (two per dot2,
       // two chains, one of them continuing the running sum)
@@ -468,6 +487,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         qf[ks + KS / 2][e] = (bf16)fmaf(bb, co, a * si);
       }
   }
+  // The queries carry scale * log2(e), rounded once more to bf16 (after any
+  // rotation, so the fused path still equals rotation followed by attention).
+#pragma unroll
+  for (int ks = 0; ks < KS; ks++)
+#pragma unroll
+    for (int e = 0; e < 8; e++) qf[ks][e] = (bf16)((float)qf[ks][e] * c_log2);
   for (int i = 0; i < steps; i += 2) {
     tile_step(tg_lo + i, std::integral_constant<int, 0>{});
     if (i + 1 < steps) tile_step(tg_lo + i + 1, std::integral_constant<int, 1>{});
@@ -487,23 +512,24 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       for (int db = 0; db < DB; db++)
 #pragma unroll
         for (int i = 0; i < 16; i++) xfer[(db * 16 + i) * 64] = o[db][i];
-      xfer[(DB * 16) * 64] = m_run;
+      xfer[(DB * 16) * 64] = lim > -1e29f ? m_ref : -1e30f;  // no visible key: weight 0 in the merge
       xfer[(DB * 16 + 1) * 64] = l_run;
     }
     __syncthreads();
     if (grp == 0) {
+      float m0 = lim > -1e29f ? m_ref : -1e30f;
 #pragma unroll
       for (int g = 1; g < KSPLIT; g++) {
         const float* xfer = xslot(g);
         const float m1 = xfer[(DB * 16) * 64], l1 = xfer[(DB * 16 + 1) * 64];
-        const float m = fmaxf(m_run, m1);
-        const float a0 = fast_exp2((m_run - m) * c_log2), a1 = fast_exp2((m1 - m) * c_log2);
+        const float m = fmaxf(m0, m1);
+        const float a0 = fast_exp2(m0 - m), a1 = fast_exp2(m1 - m);
         l_run = l_run * a0 + l1 * a1;
 #pragma unroll
         for (int db = 0; db < DB; db++)
 #pragma unroll
           for (int i = 0; i < 16; i++) o[db][i] = o[db][i] * a0 + xfer[(db * 16 + i) * 64] * a1;
-        m_run = m;
+        m0 = m;
       }
     }
     __syncthreads();  // the hand-over area is free again before any later tile load

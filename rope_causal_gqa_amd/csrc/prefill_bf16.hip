@@ -392,13 +392,29 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       }
       // mask (diagonal / tail tiles only) and row max
       if ((causal && kv0 + BN - 1 > wrow_lo + off) || kv0 + BN > nkeys || (W > 0 && kv0 <= wrow_hi + off - W)) {
+        if constexpr (MSK && !MSTAGE) {
+          // (the kernels that keep mask registers per lane: no room for the row bounds)
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; kb2++)
+          for (int kb2 = 0; kb2 < NKB; kb2++)
 #pragma unroll
-          for (int i = 0; i < 16; i++) {
-            const int key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
-            if (key >= nkeys || (causal && key > qrow + off) || (W > 0 && key <= qrow + off - W)) s[kb2][i] = -INFINITY;
-          }
+            for (int i = 0; i < 16; i++) {
+              const int key = kv0 + kb2 * 32 + 8 * (i >> 2) + 4 * hf + (i & 3);
+              if (key >= nkeys || (causal && key > qrow + off) || (W > 0 && key <= qrow + off - W))
+                s[kb2][i] = -INFINITY;
+            }
+        } else {
+          // this row sees keys base + c for lo <= c <= hi (c: the element's offset in the lane's runs)
+          const int base = kv0 + 4 * hf;
+          const int hi = (causal ? min(nkeys - 1, qrow + off) : nkeys - 1) - base;
+          const int lo = qrow + off - W + 1 - base;
+#pragma unroll
+          for (int kb2 = 0; kb2 < NKB; kb2++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) {
+              const int c = kb2 * 32 + 8 * (i >> 2) + (i & 3);
+              if (c > hi || (W > 0 && c < lo)) s[kb2][i] = -INFINITY;
+            }
+        }
       }
       float mx = s[0][0];
 #pragma unroll

@@ -18,7 +18,9 @@
  *   - All tensor pointers are DEVICE pointers owned by the caller; the library
  *     allocates nothing and frees nothing.  Its only mutable state is a
  *     per-thread memo of the last prefill grid choice (a pure function of the
- *     shape), so calls from several threads are safe.
+ *     shape) and, for attn_decode_noalloc only, a fixed 16 MiB device array per
+ *     GPU with its address cached per device; calls from several threads are
+ *     safe except overlapping attn_decode_noalloc calls on one GPU.
  *   - Tensors are dense and row-major with head_dim innermost.  Element type is
  *     selected by `dt`: RCGQA_BF16 (bfloat16 storage, fp32 arithmetic) or
  *     RCGQA_FP32.  Tensor pointers must be 16-byte aligned (the kernels move
@@ -53,7 +55,8 @@ typedef enum {
   RCGQA_OK = 0,
   RCGQA_EINVAL = 1,       /* bad argument (checked on the host, nothing launched) */
   RCGQA_EUNSUPPORTED = 2, /* valid, but no kernel for this head_dim / dtype       */
-  RCGQA_EHIP = 3          /* the HIP runtime reported an error at launch          */
+  RCGQA_EHIP = 3,         /* the HIP runtime reported an error at launch          */
+  RCGQA_ENOSPACE = 4      /* too large for the fixed scratch of attn_decode_noalloc */
 } rcgqa_status;
 
 typedef enum { RCGQA_BF16 = 0, RCGQA_FP32 = 1 } rcgqa_dtype;
@@ -263,6 +266,31 @@ rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache
                          float scale, rcgqa_dtype dt,
                          void* workspace, size_t workspace_bytes,
                          rcgqa_stream stream);
+
+/*
+ * attn_decode_noalloc -- attn_decode without a workspace argument, for callers
+ * that cannot allocate device memory (code under HIP graph capture, serving
+ * loops, harnesses that forbid allocation).  Same arguments, result and
+ * kernels as attn_decode (bit-identical output); the split-K partial states
+ * go to a fixed array of 16 MiB that the library holds on every GPU it runs
+ * on until the process ends.  The call itself allocates and frees nothing.
+ *
+ * Limit: the partial states must fit in 16 MiB, i.e.
+ *   B * Hq * ceil(max_kv / 2048) * (head_dim + 2) * 4 bytes for RCGQA_BF16,
+ *   B * Hq * ceil(max_kv / 256)  * (head_dim + 2) * 4 bytes for RCGQA_FP32;
+ * larger problems return RCGQA_ENOSPACE and launch nothing (the B=64 Hq=64
+ * head_dim=128 max_kv=8193 bf16 decode needs 10.6 MB).  The array needs no
+ * initial contents and every call overwrites what it reads.
+ * The array is found for the calling thread's current device (hipGetDevice),
+ * so `stream` must belong to that device.  All calls on one GPU share its
+ * array: calls that overlap in time on one GPU (different streams or threads)
+ * race and give wrong results; serialise them, or use attn_decode with
+ * separate workspaces.
+ */
+rcgqa_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache,
+                                 const int32_t* kv_lens, void* out,
+                                 int B, int Hq, int Hkv, int head_dim, int max_kv,
+                                 float scale, rcgqa_dtype dt, rcgqa_stream stream);
 
 /*
  * kv_append -- write one new key row and value row per sequence into the cache.

@@ -11,7 +11,7 @@ import os
 LIB_NAME = "librcgqa.so"
 _HERE = os.path.dirname(os.path.abspath(__file__))
 
-OK, EINVAL, EUNSUPPORTED, EHIP = 0, 1, 2, 3
+OK, EINVAL, EUNSUPPORTED, EHIP, ENOSPACE = 0, 1, 2, 3, 4
 BF16, FP32 = 0, 1
 
 _lib = None
@@ -50,6 +50,8 @@ def lib():
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
     L.attn_decode.restype = i32
+    L.attn_decode_noalloc.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp]
+    L.attn_decode_noalloc.restype = i32
     L.kv_append.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, vp]
     L.kv_append.restype = i32
     L.rope_attn_prefill_workspace_bytes.argtypes = [i32, i32, i32]
@@ -76,7 +78,7 @@ def _check(status, what):
     if status == OK:
         return
     msg = lib().rcgqa_status_string(status).decode()
-    if status == EINVAL:
+    if status in (EINVAL, ENOSPACE):
         raise ValueError(f"{what}: {msg}")
     if status == EUNSUPPORTED:
         raise NotImplementedError(f"{what}: {msg}")
@@ -247,6 +249,23 @@ def attn_decode(q, k_cache, v_cache, kv_lens, out=None, scale=None, workspace=No
                            _dev(out, "out", dt, 3), B, Hq, Hkv, D, max_kv, float(scale), dt,
                            _dev(workspace, "workspace"), wbytes, _stream(q))
     _check(st, "attn_decode")
+    return out
+
+
+def attn_decode_noalloc(q, k_cache, v_cache, kv_lens, out, scale):
+    """attn_decode with the split-K partial states in the library's fixed per-GPU
+    scratch (no workspace, no allocation inside the call; see rcgqa.h)."""
+    dt = _dtype_code(q)
+    B, Hq, D = q.shape
+    _, Hkv, max_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, max_kv, D) or tuple(v_cache.shape) != (B, Hkv, max_kv, D):
+        raise ValueError("caches must be [B, Hkv, max_kv, D] matching q")
+    if tuple(out.shape) != (B, Hq, D):
+        raise ValueError("out must be [B, Hq, D]")
+    st = lib().attn_decode_noalloc(_dev(q, "q", dt, 3), _dev(k_cache, "k_cache", dt, 4),
+                                   _dev(v_cache, "v_cache", dt, 4), _i32(kv_lens, "kv_lens", B),
+                                   _dev(out, "out", dt, 3), B, Hq, Hkv, D, max_kv, float(scale), dt, _stream(q))
+    _check(st, "attn_decode_noalloc")
     return out
 
 

@@ -74,6 +74,7 @@ const char* rcgqa_status_string(rcgqa_status s) {
     case RCGQA_EINVAL: return "invalid argument";
     case RCGQA_EUNSUPPORTED: return "unsupported head_dim or dtype";
     case RCGQA_EHIP: return "HIP runtime error at launch";
+    case RCGQA_ENOSPACE: return "problem needs more than the library's fixed scratch (use the workspace entry point)";
   }
   return "unknown status";
 }
@@ -240,6 +241,24 @@ rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache
   if (workspace_bytes < rcgqa::decode_workspace_bytes(B, Hq, head_dim, max_kv)) return RCGQA_EINVAL;
   return hip_status(rcgqa::launch_decode(q, k_cache, v_cache, kv_lens, out, B, Hq, Hkv, head_dim, max_kv, scale,
                                          dt == RCGQA_BF16, workspace, (hipStream_t)stream));
+}
+
+rcgqa_status attn_decode_noalloc(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_lens,
+                                 void* out, int B, int Hq, int Hkv, int head_dim, int max_kv, float scale,
+                                 rcgqa_dtype dt, rcgqa_stream stream) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !out || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!al16({q, k_cache, v_cache, out}) || !al4(kv_lens)) return RCGQA_EINVAL;
+  if (out == q || out == k_cache || out == v_cache) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || Hq / Hkv > 16 || B > 65535 || Hq > 65535) return RCGQA_EUNSUPPORTED;
+  const bool bf16 = dt == RCGQA_BF16;
+  if (rcgqa::decode_scratch_bytes(B, Hq, head_dim, max_kv, bf16) > rcgqa::kDecodeNoAllocBytes) return RCGQA_ENOSPACE;
+  void* ws = nullptr;
+  if (rcgqa::decode_noalloc_scratch(&ws) != hipSuccess) return RCGQA_EHIP;
+  return hip_status(rcgqa::launch_decode(q, k_cache, v_cache, kv_lens, out, B, Hq, Hkv, head_dim, max_kv, scale,
+                                         bf16, ws, (hipStream_t)stream));
 }
 
 size_t rope_attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv) {

@@ -12,6 +12,8 @@
 //     M = max_c m_c,  out = sum_c e^(m_c - M) acc_c / sum_c e^(m_c - M) l_c.
 // The split is what lets short and long sequences share the GPU evenly; the
 // fixed merge order keeps results bitwise repeatable.
+#include <mutex>
+
 #include "common.h"
 #include "launch.h"
 
@@ -401,6 +403,41 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
     else launch_decode_t<float, 128>(q, kc, vc, kv_lens, out, B, Hq, Hkv, max_kv, scale, ws, st);
   }
   return hipGetLastError();
+}
+
+// Scratch of the no-allocation decode entry point: the split-K partial states
+// live in this fixed array instead of a caller-owned workspace.  Every GPU the
+// library runs on holds its own copy for the life of the process.  In host
+// code `scratch` names a host-side stand-in, never a device address: the
+// device address is looked up once per device and only that pointer is used.
+static __device__ __align__(256) float scratch[kDecodeNoAllocBytes / sizeof(float)];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_dev[kMaxDevices] = {};
+}  // namespace
+
+size_t decode_scratch_bytes(int B, int Hq, int D, int max_kv, bool bf16_io) {
+  const size_t per = bf16_io ? KCH : KC;  // keys per partial state in the bf16 / fp32 pass
+  const size_t n = ((size_t)max_kv + per - 1) / per;
+  return (size_t)B * Hq * n * (size_t)(D + 2) * sizeof(float);
+}
+
+hipError_t decode_noalloc_scratch(void** ptr) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_dev[dev]) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));  // the current device's copy
+    if (e != hipSuccess) return e;
+    g_scratch_dev[dev] = p;
+  }
+  *ptr = g_scratch_dev[dev];
+  return hipSuccess;
 }
 
 // Cache append: block (b, kv head) copies one row of k_new and v_new into

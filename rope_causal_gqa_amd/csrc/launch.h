@@ -57,6 +57,14 @@ hipError_t launch_decode(const void* q, const void* kc, const void* vc, const in
                          int B, int Hq, int Hkv, int D, int max_kv, float scale, bool bf16, void* ws,
                          hipStream_t st);
 
+// The no-allocation decode: partial states in a fixed per-device array of
+// kDecodeNoAllocBytes.  decode_scratch_bytes is what launch_decode uses of a
+// workspace for these sizes and element type; decode_noalloc_scratch returns
+// the current device's array (looked up once per device).
+constexpr size_t kDecodeNoAllocBytes = (size_t)16 << 20;
+size_t decode_scratch_bytes(int B, int Hq, int D, int max_kv, bool bf16_io);
+hipError_t decode_noalloc_scratch(void** ptr);
+
 hipError_t launch_kv_append(void* kc, void* vc, const void* kn, const void* vn, const int32_t* slots, int B,
                             int Hkv, int D, int max_kv, bool bf16, hipStream_t st);
 

@@ -39,6 +39,7 @@ def test_status_strings():
     assert L.rcgqa_status_string(1) == b"invalid argument"
     assert L.rcgqa_status_string(2).startswith(b"unsupported")
     assert L.rcgqa_status_string(3).startswith(b"HIP")
+    assert b"scratch" in L.rcgqa_status_string(4)
     assert L.rcgqa_status_string(99) == b"unknown status"
 
 
@@ -124,6 +125,42 @@ def test_decode_rejects(args):
     st = R.lib().attn_decode(FAKE, FAKE, FAKE, a["lens"], ctypes.c_void_p(8192), a["B"], a["Hq"], a["Hkv"], a["D"],
                              a["max_kv"], a["scale"], 0, ws, a["wbytes"], None)
     assert st == BD.EINVAL
+
+
+def test_decode_noalloc_rejects_aliased_output():
+    q, k, v = (ctypes.c_void_p(4096 * i) for i in (3, 4, 5))
+    for out in (q, k, v):
+        assert R.lib().attn_decode_noalloc(q, k, v, FAKE, out, 1, 8, 2, 128, 10, 0.1, 0, None) == BD.EINVAL
+
+
+@pytest.mark.parametrize("args", [
+    dict(Hq=12, Hkv=8), dict(max_kv=0), dict(scale=-1.0), dict(scale=float("nan")), dict(lens=None), dict(D=63),
+    dict(B=0), dict(dt=7),
+])
+def test_decode_noalloc_rejects(args):
+    a = dict(B=2, Hq=8, Hkv=2, D=128, max_kv=300, scale=0.1, lens=FAKE, dt=0)
+    a.update(args)
+    st = R.lib().attn_decode_noalloc(FAKE, FAKE, FAKE, a["lens"], ctypes.c_void_p(8192), a["B"], a["Hq"], a["Hkv"],
+                                     a["D"], a["max_kv"], a["scale"], a["dt"], None)
+    assert st == BD.EINVAL
+
+
+@pytest.mark.parametrize("B,Hq,D,max_kv,dt,fits", [
+    (64, 64, 128, 8193, 0, True),     # the B=64 Hq=64 decode workload: 10.6 MB of partial states
+    (64, 64, 128, 14336, 0, True),    # 7 splits of 2048 keys: 14.9 MB
+    (64, 64, 128, 16385, 0, False),   # 9 splits: 19.2 MB > 16 MiB
+    (64, 64, 128, 1792, 1, True),     # fp32 keeps a partial state per 256 keys: 7 of them, 14.9 MB
+    (64, 64, 128, 2048, 1, False),    # 8 fp32 partial states: 17.0 MB
+])
+def test_decode_noalloc_limit(B, Hq, D, max_kv, dt, fits):
+    """The size rule of the fixed scratch, checked on the host before any launch."""
+    per = 2048 if dt == 0 else 256
+    need = B * Hq * (-(-max_kv // per)) * (D + 2) * 4
+    assert (need <= 16 << 20) == fits
+    if not fits:
+        st = R.lib().attn_decode_noalloc(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(8192), B, Hq, 8, D, max_kv, 0.1, dt,
+                                         None)
+        assert st == BD.ENOSPACE
 
 
 def test_decode_unsupported_group():

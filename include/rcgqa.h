@@ -256,7 +256,8 @@ size_t attn_decode_workspace_bytes(int B, int Hq, int head_dim, int max_kv);
  *            head_dim, max_kv) bytes, 256-byte aligned, owned by the caller;
  *            no initial contents are required.  Concurrent calls must not
  *            share a workspace.
- * head_dim: 64 or 128.  Hq % Hkv == 0, Hq/Hkv <= 16.
+ * head_dim: 64 or 128.  Hq % Hkv == 0, Hq/Hkv <= 16.  out must not alias q or
+ * the caches.
  * The result does not depend on the order in which partial states finish:
  * partial states are merged in a fixed order (bitwise repeatable).
  */

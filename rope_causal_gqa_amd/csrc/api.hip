@@ -233,6 +233,7 @@ rcgqa_status attn_decode(const void* q, const void* k_cache, const void* v_cache
                          rcgqa_dtype dt, void* workspace, size_t workspace_bytes, rcgqa_stream stream) {
   if (!q || !k_cache || !v_cache || !kv_lens || !out || !workspace || !good_dtype(dt)) return RCGQA_EINVAL;
   if (!al16({q, k_cache, v_cache, out}) || !al4(kv_lens)) return RCGQA_EINVAL;
+  if (out == q || out == k_cache || out == v_cache) return RCGQA_EINVAL;
   if (!pos_int(B) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv)) return RCGQA_EINVAL;
   if (head_dim < 2 || head_dim % 2 || !finite_pos(scale)) return RCGQA_EINVAL;
   if (mul({B, Hkv, max_kv, head_dim}) < 0) return RCGQA_EINVAL;

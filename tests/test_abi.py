@@ -127,9 +127,11 @@ def test_decode_rejects(args):
     assert st == BD.EINVAL
 
 
-def test_decode_noalloc_rejects_aliased_output():
+def test_decode_rejects_aliased_output():
+    ws = ctypes.c_void_p(4096 * 16)
     q, k, v = (ctypes.c_void_p(4096 * i) for i in (3, 4, 5))
     for out in (q, k, v):
+        assert R.lib().attn_decode(q, k, v, FAKE, out, 1, 8, 2, 128, 10, 0.1, 0, ws, 1 << 30, None) == BD.EINVAL
         assert R.lib().attn_decode_noalloc(q, k, v, FAKE, out, 1, 8, 2, 128, 10, 0.1, 0, None) == BD.EINVAL
 
 

@@ -129,21 +129,12 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 //   S^T (32 keys x 16 heads) = K Q^T   v_mfma_f32_16x16x32_bf16, K from LDS
 //   O^T (D x 16 heads)      += V^T P^T  same MFMA, V^T via the LDS transpose read
 // In both outputs a lane owns one head (lane % 16), so the online-softmax
-// rescale is one multiply per accumulator.  The 4 waves' states are combined
+// rescale is one multiply per accumulator.  The DW waves' states are combined
 // in LDS and written as one partial state per (split, head).
-#ifndef RCGQA_DECODE_SPLIT
-#define RCGQA_DECODE_SPLIT 2048
-#endif
-#ifndef RCGQA_DECODE_NT
-#define RCGQA_DECODE_NT 1
-#endif
-#ifndef RCGQA_DECODE_WAVES
-#define RCGQA_DECODE_WAVES 8
-#endif
 namespace {
-constexpr int KCH = RCGQA_DECODE_SPLIT;  // keys per split (>= KC, so the workspace bound holds)
-constexpr int TK = 32;                   // keys per wave tile
-constexpr int DW = RCGQA_DECODE_WAVES;   // waves per workgroup
+constexpr int KCH = 2048;  // keys per split (>= KC, so the workspace bound holds)
+constexpr int TK = 32;     // keys per wave tile
+constexpr int DW = 8;      // waves per workgroup
 static_assert(KCH >= KC && KCH % TK == 0, "split must be a multiple of the tile and at least KC");
 }
 
@@ -201,13 +192,8 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
       const int idx = p * 64 + lane, r = idx / CH, c = idx - r * CH;
       const int key = t0 + r;
       if (key < kend) {
-#if RCGQA_DECODE_NT
         pk[p] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(kb + (size_t)key * D) + c);
         pv[p] = __builtin_nontemporal_load(reinterpret_cast<const bf16x8*>(vb + (size_t)key * D) + c);
-#else
-        pk[p] = reinterpret_cast<const bf16x8*>(kb + (size_t)key * D)[c];
-        pv[p] = reinterpret_cast<const bf16x8*>(vb + (size_t)key * D)[c];
-#endif
       } else {
         pk[p] = bf16x8{};
         pv[p] = bf16x8{};
@@ -266,15 +252,16 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
     mx = half_swap_max(mx);
     const float m_new = fmaxf(m_run, mx);  // finite: every tile holds a valid key
     const float alpha = fast_exp2(m_run - m_new);
+    // weights rounded to bf16 for the P.V product; the row sum adds those
+    // same rounded weights, so the normaliser matches what was accumulated
     bf16x8 pf;
     float psum = 0.f;
 #pragma unroll
     for (int kb2 = 0; kb2 < 2; kb2++) {
 #pragma unroll
       for (int j = 0; j < 4; j++) {
-        const float p = fast_exp2(s[kb2][j] - m_new);
-        psum += p;
-        pf[4 * kb2 + j] = (bf16)p;
+        pf[4 * kb2 + j] = (bf16)fast_exp2(s[kb2][j] - m_new);
+        psum += (float)pf[4 * kb2 + j];
       }
     }
     l_run = l_run * alpha + psum;
@@ -294,10 +281,13 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
   l_run += __shfl_xor(l_run, 16);
   l_run = half_swap_sum(l_run);
 
-  // combine the waves in LDS: [w][16 heads][D + 2] fp32
+  // combine the waves in LDS: [w][16 heads][D + 3] fp32 (m, l, acc[D], one
+  // pad: with an odd row stride the 64 lanes (head n, lane group g) of each
+  // store land on at most two per bank; the readers take consecutive columns)
   __syncthreads();
   float* st = reinterpret_cast<float*>(lds);
-  constexpr int SR = D + 2;
+  constexpr int SR = D + 3;
+  static_assert(DW * 16 * SR * sizeof(float) <= sizeof(lds), "combine area");
   float* mine = st + (w * 16 + n) * SR;
   if (g == 0) {
     mine[0] = m_run;

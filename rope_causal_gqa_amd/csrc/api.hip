@@ -178,6 +178,10 @@ rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* 
     return RCGQA_EINVAL;
   if (!attn_head_dim(head_dim) || !prefill_grid_ok(B, Hq, Sq)) return RCGQA_EUNSUPPORTED;
   const hipStream_t st = (hipStream_t)stream;
+  // A window of max_kv or more excludes no key (a query sits at a position
+  // below max_kv), so it is no window; this also keeps the kernels' position
+  // arithmetic (position - window) far from int32 overflow.
+  if (window >= max_kv) window = 0;
   // caches [B, Hkv, max_kv, D]: rows of one (batch, KV head) are contiguous
   const rcgqa::KvSpec kv{(long long)Hkv * max_kv * head_dim, (long long)max_kv * head_dim, head_dim, kv_lens,
                          max_kv, window};

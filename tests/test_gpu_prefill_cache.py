@@ -44,6 +44,7 @@ CASES = [
     (2, 300, 8, 2, 128, 1100, [300, 1000], 1, 64, "bf16"),     # sliding window
     (1, 129, 4, 1, 64, 129, [129], 1, 1, "bf16"),              # window 1: own value
     (2, 200, 4, 2, 128, 400, [260, 400], 1, 5000, "bf16"),     # window longer than the cache
+    (2, 200, 4, 2, 128, 400, [10, 400], 1, 2147483647, "bf16"),  # int32-max window, fewer keys than queries
     (2, 1, 16, 2, 128, 700, [513, 700], 1, 0, "bf16"),         # one token: a decode step
     (1, 513, 2, 1, 128, 1500, [1500], 1, 300, "bf16"),         # window with tile-unaligned edges
     (1, 2100, 8, 1, 128, 3000, [2900], 1, 0, "bf16"),          # four key groups over 64-row tiles
@@ -72,17 +73,16 @@ def test_prefill_cache_parity(B, Sq, Hq, Hkv, D, max_kv, lens, causal, window, d
     (2, 2048, 64, 8, 128, [2048, 4000], 1024),   # 4-wave kernel, short sliding window
     (2, 2048, 64, 8, 128, [2048, 4000], 2500),   # 8-wave kernel, sliding window
 ])
-def test_prefill_cache_large_sampled(B, Sq, Hq, Hkv, D, lens, window):
+def test_prefill_cache_large_all_heads(B, Sq, Hq, Hkv, D, lens, window):
     announce(f"prefill_cache large B={B} Sq={Sq} Hq={Hq} lens={lens} window={window}")
     max_kv = max(lens)
     q, kc, vc = _case(91 + window, B, Sq, Hq, Hkv, D, max_kv, "bf16")
     got = _run(q, kc, vc, lens, 1, window, "bf16", D)
-    heads = [(0, 0), (0, 37), (1, 63), (1, 8)]
     ref = oracle.attention_cache(W.to_f64(q, "bf16"), W.to_f64(kc, "bf16"), W.to_f64(vc, "bf16"), np.array(lens),
-                                 True, 1.0 / math.sqrt(D), window=window, heads=heads)
-    for b, h in heads:
-        check(got[b, :, h], ref[b, :, h], "bf16", f"large b={b} h={h}")
-    assert np.all(np.isfinite(got))
+                                 True, 1.0 / math.sqrt(D), window=window)
+    for b in range(B):
+        for h in range(Hq):
+            check(got[b, :, h], ref[b, :, h], "bf16", f"large b={b} h={h}")
 
 
 @pytest.mark.parametrize("B,S,Hq,Hkv,D,dtype", [(2, 130, 8, 2, 128, "bf16"), (2, 1000, 64, 8, 128, "bf16"),
@@ -112,8 +112,8 @@ def test_single_token_matches_decode():
     q, kc, vc = _case(77, B, 1, Hq, Hkv, D, max_kv, "bf16")
     lens = torch.tensor([1, 64, 511, 900], dtype=torch.int32, device="cuda")
     qd, kd, vd = dev(q, "bf16"), dev(kc, "bf16"), dev(vc, "bf16")
-    a = R.attn_prefill_cache(qd, kd, vd, lens, causal=True)
-    d = R.attn_decode(qd.view(B, Hq, D), kd, vd, lens)
+    a = R.attn_prefill_cache(qd, kd, vd, lens, causal=True, scale=D ** -0.5)
+    d = R.attn_decode(qd.view(B, Hq, D), kd, vd, lens, scale=D ** -0.5)
     torch.cuda.synchronize()
     check(host64(a)[:, 0], host64(d), "bf16", "prefill_cache(Sq=1) vs decode")
 
@@ -124,8 +124,8 @@ def test_prefill_cache_deterministic():
     q, kc, vc = _case(5, B, Sq, Hq, Hkv, D, max_kv, "bf16")
     qd, kd, vd = dev(q, "bf16"), dev(kc, "bf16"), dev(vc, "bf16")
     lens = torch.tensor([3000, 1700], dtype=torch.int32, device="cuda")
-    ref = R.attn_prefill_cache(qd, kd, vd, lens, window=700)
+    ref = R.attn_prefill_cache(qd, kd, vd, lens, scale=D ** -0.5, window=700)
     for _ in range(3):
-        again = R.attn_prefill_cache(qd, kd, vd, lens, window=700)
+        again = R.attn_prefill_cache(qd, kd, vd, lens, scale=D ** -0.5, window=700)
         torch.cuda.synchronize()
         assert torch.equal(again, ref)

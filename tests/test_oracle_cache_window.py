@@ -92,6 +92,19 @@ def test_window_special_cases():
         oracle.attention(q, k, v, False, 0.5, window=3)
 
 
+def test_window_int32_max_is_no_window():
+    """A window of 2^31 - 1 keys excludes nothing, also for a chunk longer than
+    the cache (rows before the first key stay zero rows)."""
+    B, Sq, Hq, Hkv, D, max_kv = 2, 12, 4, 2, 8, 9
+    q, k, v = _qkv(33, B, Sq, max_kv, Hq, Hkv, D)
+    kc, vc = _to_cache(k, max_kv), _to_cache(v, max_kv)
+    lens = np.array([5, 9])
+    big = oracle.attention_cache(q, kc, vc, lens, True, 0.4, window=2 ** 31 - 1)
+    none = oracle.attention_cache(q, kc, vc, lens, True, 0.4, window=0)
+    np.testing.assert_array_equal(big, none)
+    assert np.all(big[0, :Sq - 5] == 0.0)
+
+
 @pytest.mark.parametrize("W", [0, 5])
 def test_cache_full_chunk_equals_prefill(W):
     B, S, Hq, Hkv, D, max_kv = 2, 20, 4, 2, 8, 31

@@ -1,7 +1,8 @@
 """ctypes binding over librcgqa.so (the C ABI in include/rcgqa.h).
 
 Argument marshalling only: shapes and device pointers are read off torch
-tensors and handed to the library, which runs every step in its own HIP
+tensors and handed to the library (the attention scale is always the
+caller's: no default is computed here), which runs every step in its own HIP
 kernels on the caller's current stream.  There is no fallback: if the library
 is missing or a tensor is not a CUDA (HIP) tensor, the call raises.
 """
@@ -156,7 +157,7 @@ def rope_apply_interleaved(q, k, position_ids=None, theta=10000.0, linear_factor
     return _rope("rope_apply_interleaved", q, k, position_ids, theta, linear_factor)
 
 
-def attn_prefill(q, k, v, out=None, causal=True, scale=None):
+def attn_prefill(q, k, v, out=None, causal=True, *, scale):
     """out [B,S,Hq,D] = attention(q [B,S,Hq,D], k/v [B,S,Hkv,D]) (see rcgqa.h)."""
     import torch
     dt = _dtype_code(q)
@@ -168,7 +169,6 @@ def attn_prefill(q, k, v, out=None, causal=True, scale=None):
         out = torch.empty_like(q)
     if tuple(out.shape) != (B, S, Hq, D):
         raise ValueError("out must be [B, S, Hq, D]")
-    scale = D ** -0.5 if scale is None else scale
     st = lib().attn_prefill(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), _dev(v, "v", dt, 4),
                             _dev(out, "out", dt, 4), B, S, Hq, Hkv, D, int(bool(causal)),
                             float(scale), dt, _stream(q))
@@ -176,7 +176,7 @@ def attn_prefill(q, k, v, out=None, causal=True, scale=None):
     return out
 
 
-def attn_prefill_masked(q, k, v, mask, out=None, causal=False, scale=None):
+def attn_prefill_masked(q, k, v, mask, out=None, causal=False, *, scale):
     """attn_prefill plus an additive mask [B, 1 or Hq, S, L >= S] of the run dtype (see rcgqa.h)."""
     import torch
     dt = _dtype_code(q)
@@ -191,7 +191,6 @@ def attn_prefill_masked(q, k, v, mask, out=None, causal=False, scale=None):
         out = torch.empty_like(q)
     if tuple(out.shape) != (B, S, Hq, D):
         raise ValueError("out must be [B, S, Hq, D]")
-    scale = D ** -0.5 if scale is None else scale
     st = lib().attn_prefill_masked(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), _dev(v, "v", dt, 4),
                                    _dev(mask, "mask", dt, 4), _dev(out, "out", dt, 4), B, S, Hq, Hkv, D,
                                    int(mask.shape[1]), int(mask.shape[3]), int(bool(causal)), float(scale), dt,
@@ -200,7 +199,7 @@ def attn_prefill_masked(q, k, v, mask, out=None, causal=False, scale=None):
     return out
 
 
-def attn_prefill_cache(q, k_cache, v_cache, kv_lens, out=None, causal=True, scale=None, window=0):
+def attn_prefill_cache(q, k_cache, v_cache, kv_lens, out=None, causal=True, *, scale, window=0):
     """out [B,Sq,Hq,D] = attention of the Sq newest tokens q [B,Sq,Hq,D] of each
     sequence over its kv_lens[b] cached rows (caches [B,Hkv,max_kv,D]); with
     ``window`` > 0 a token sees only its ``window`` most recent positions."""
@@ -214,7 +213,6 @@ def attn_prefill_cache(q, k_cache, v_cache, kv_lens, out=None, causal=True, scal
         out = torch.empty_like(q)
     if tuple(out.shape) != (B, Sq, Hq, D):
         raise ValueError("out must be [B, Sq, Hq, D]")
-    scale = D ** -0.5 if scale is None else scale
     st = lib().attn_prefill_cache(_dev(q, "q", dt, 4), _dev(k_cache, "k_cache", dt, 4),
                                   _dev(v_cache, "v_cache", dt, 4), _i32(kv_lens, "kv_lens", B),
                                   _dev(out, "out", dt, 4), B, Sq, Hq, Hkv, D, max_kv, int(bool(causal)),
@@ -227,7 +225,7 @@ def attn_decode_workspace_bytes(B, Hq, head_dim, max_kv):
     return int(lib().attn_decode_workspace_bytes(B, Hq, head_dim, max_kv))
 
 
-def attn_decode(q, k_cache, v_cache, kv_lens, out=None, scale=None, workspace=None):
+def attn_decode(q, k_cache, v_cache, kv_lens, out=None, *, scale, workspace=None):
     """out [B,Hq,D] = decode attention of q [B,Hq,D] over caches [B,Hkv,max_kv,D]."""
     import torch
     dt = _dtype_code(q)
@@ -243,7 +241,6 @@ def attn_decode(q, k_cache, v_cache, kv_lens, out=None, scale=None, workspace=No
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     wbytes = workspace.numel() * workspace.element_size()
-    scale = D ** -0.5 if scale is None else scale
     st = lib().attn_decode(_dev(q, "q", dt, 3), _dev(k_cache, "k_cache", dt, 4),
                            _dev(v_cache, "v_cache", dt, 4), _i32(kv_lens, "kv_lens", B),
                            _dev(out, "out", dt, 3), B, Hq, Hkv, D, max_kv, float(scale), dt,
@@ -295,7 +292,7 @@ def rope_attn_prefill_workspace_bytes(B, S, head_dim):
     return int(lib().rope_attn_prefill_workspace_bytes(B, S, head_dim))
 
 
-def rope_attn_prefill(q, k, v, position_ids=None, out=None, causal=True, scale=None, theta=10000.0,
+def rope_attn_prefill(q, k, v, position_ids=None, out=None, causal=True, *, scale, theta=10000.0,
                       linear_factor=1.0, workspace=None):
     """out [B,S,Hq,D] = attention(rope(q), rope(k), v); k is rotated in place,
     q is left as it is (see rcgqa.h)."""
@@ -311,7 +308,6 @@ def rope_attn_prefill(q, k, v, position_ids=None, out=None, causal=True, scale=N
         raise ValueError("out must be [B, S, Hq, D]")
     pos = ctypes.c_void_p(0) if position_ids is None else _i32(position_ids, "position_ids", B * S)
     workspace, wbytes = _workspace(rope_attn_prefill_workspace_bytes(B, S, D), q, workspace)
-    scale = D ** -0.5 if scale is None else scale
     st = lib().rope_attn_prefill(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), _dev(v, "v", dt, 4),
                                  _dev(out, "out", dt, 4), pos, B, S, Hq, Hkv, D, int(bool(causal)), float(scale),
                                  float(theta), float(linear_factor), dt, _dev(workspace, "workspace"), wbytes,
@@ -324,7 +320,7 @@ def rope_attn_decode_workspace_bytes(B, Hq, head_dim, max_kv):
     return int(lib().rope_attn_decode_workspace_bytes(B, Hq, head_dim, max_kv))
 
 
-def rope_attn_decode(q, k_new, v_new, k_cache, v_cache, kv_lens, position_ids=None, out=None, scale=None,
+def rope_attn_decode(q, k_new, v_new, k_cache, v_cache, kv_lens, position_ids=None, out=None, *, scale,
                      theta=10000.0, linear_factor=1.0, workspace=None):
     """One decode step: rotate q [B,Hq,D] and k_new [B,Hkv,D], append k_new/v_new at row
     kv_lens[b]-1 of the caches [B,Hkv,max_kv,D], attend (see rcgqa.h)."""
@@ -342,7 +338,6 @@ def rope_attn_decode(q, k_new, v_new, k_cache, v_cache, kv_lens, position_ids=No
         raise ValueError("out must be [B, Hq, D]")
     pos = ctypes.c_void_p(0) if position_ids is None else _i32(position_ids, "position_ids", B)
     workspace, wbytes = _workspace(rope_attn_decode_workspace_bytes(B, Hq, D, max_kv), q, workspace)
-    scale = D ** -0.5 if scale is None else scale
     st = lib().rope_attn_decode(_dev(q, "q", dt, 3), _dev(k_new, "k_new", dt, 3), _dev(v_new, "v_new", dt, 3),
                                 _dev(k_cache, "k_cache", dt, 4), _dev(v_cache, "v_cache", dt, 4),
                                 _i32(kv_lens, "kv_lens", B), pos, _dev(out, "out", dt, 3), B, Hq, Hkv, D, max_kv,

@@ -236,9 +236,9 @@ def test_binding_requires_device_tensors():
     with pytest.raises(ValueError):
         R.rope_apply(q, q.clone())
     with pytest.raises(ValueError):
-        R.attn_prefill(q, q, q)
+        R.attn_prefill(q, q, q, scale=0.125)
     with pytest.raises(ValueError):
-        R.attn_prefill_cache(q, q, q, torch.zeros(1, dtype=torch.int32))
+        R.attn_prefill_cache(q, q, q, torch.zeros(1, dtype=torch.int32), scale=0.125)
 
 
 def test_fused_workspace_bytes():
@@ -298,10 +298,11 @@ def test_fused_binding_requires_device_tensors():
     torch = pytest.importorskip("torch")
     q = torch.zeros(1, 4, 2, 64)
     with pytest.raises(ValueError):
-        R.rope_attn_prefill(q, q.clone(), q.clone())
+        R.rope_attn_prefill(q, q.clone(), q.clone(), scale=0.125)
     with pytest.raises(ValueError):
         R.rope_attn_decode(torch.zeros(1, 2, 64), torch.zeros(1, 1, 64), torch.zeros(1, 1, 64),
-                           torch.zeros(1, 1, 8, 64), torch.zeros(1, 1, 8, 64), torch.ones(1, dtype=torch.int32))
+                           torch.zeros(1, 1, 8, 64), torch.zeros(1, 1, 8, 64), torch.ones(1, dtype=torch.int32),
+                           scale=0.125)
 
 
 @pytest.mark.parametrize("theta,D,alpha", [(1e4, 128, 8.0), (5e5, 64, 2.5), (1e4, 4, 4.0), (100.0, 256, 0.5),

@@ -102,8 +102,8 @@ def test_decode_deterministic_and_workspace_reuse():
     vc = dev(W.random_case(3, (B, Hkv, max_kv, D), "bf16"), "bf16")
     lens = _i32([3000, 1, 2048, 777])
     ws = torch.full((R.attn_decode_workspace_bytes(B, Hq, D, max_kv),), 255, dtype=torch.uint8, device="cuda")
-    a = R.attn_decode(q, kc, vc, lens, workspace=ws)
-    b = R.attn_decode(q, kc, vc, lens, workspace=ws)
+    a = R.attn_decode(q, kc, vc, lens, scale=D ** -0.5, workspace=ws)
+    b = R.attn_decode(q, kc, vc, lens, scale=D ** -0.5, workspace=ws)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
 

@@ -123,9 +123,9 @@ def test_masked_prefill_bitwise_pins(B, S, Hq, Hkv, same_split):
     zero = torch.zeros((B, 1, S, S), dtype=torch.bfloat16, device="cuda")
     tri = torch.triu(torch.full((S, S), float("-inf"), device="cuda"), diagonal=1).to(torch.bfloat16)
     tri = tri.expand(B, 1, S, S).contiguous()
-    ref = R.attn_prefill(q, k, v, causal=True)
-    got0 = R.attn_prefill_masked(q, k, v, zero, causal=True)
-    got1 = R.attn_prefill_masked(q, k, v, tri, causal=False)
+    ref = R.attn_prefill(q, k, v, causal=True, scale=D ** -0.5)
+    got0 = R.attn_prefill_masked(q, k, v, zero, causal=True, scale=D ** -0.5)
+    got1 = R.attn_prefill_masked(q, k, v, tri, causal=False, scale=D ** -0.5)
     torch.cuda.synchronize()
     assert torch.equal(got0, ref), "zero mask changes the causal result"
     if same_split:

@@ -175,6 +175,7 @@ def test_decode_lengths_are_clamped():
     kc, vc = r.standard_normal((B, Hkv, max_kv, D)), r.standard_normal((B, Hkv, max_kv, D))
     out = oracle.decode(q, kc, vc, np.array([0, 99]), 1.0)
     assert np.all(out[0] == 0.0)
+    assert np.all(oracle.decode(q, kc, vc, np.array([-3, 99]), 1.0)[0] == 0.0)   # negative: no keys
     np.testing.assert_array_equal(out[1], oracle.decode(q, kc, vc, np.array([0, max_kv]), 1.0)[1])
 
 

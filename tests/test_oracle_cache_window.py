@@ -144,6 +144,8 @@ def test_cache_variable_lengths_and_degenerate_rows():
     lens = np.array([0, 3, 6, 99])                    # 99 is clamped to max_kv
     got = oracle.attention_cache(q, kc, vc, lens, True, 1.0)
     assert np.all(got[0] == 0.0)                      # empty cache: zero rows
+    neg = oracle.attention_cache(q, kc, vc, np.array([-4, 3, 6, 99]), True, 1.0)
+    assert np.all(neg[0] == 0.0)                      # a negative length is an empty cache
     assert np.all(got[1, :3] == 0.0)                  # queries before the first key see nothing
     for b, L in [(1, 3), (2, 6), (3, max_kv)]:
         n = min(Sq, L)

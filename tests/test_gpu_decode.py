@@ -62,6 +62,7 @@ DEC_EDGE = [
     (3, 16, 8, 128, 1025, [1024, 1025, 513], "bf16"),
     (2, 8, 8, 64, 700, [700, 2], "bf16"),
     (2, 16, 1, 128, 300, [0, 1000], "bf16"),          # empty row and clamped length
+    (3, 16, 1, 128, 300, [-5, 299, 0], "bf16"),       # negative length: an empty cache
     (5, 32, 2, 128, 2049, [2049, 7, 1536, 100, 1], "bf16"),
     (2, 8, 1, 128, 20000, [20000, 6145], "bf16"),     # > 8 splits: merge batches
     (2, 16, 1, 128, 4096, [4096, 2048], "bf16"),      # exact split multiples

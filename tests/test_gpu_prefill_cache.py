@@ -40,6 +40,7 @@ CASES = [
     (2, 100, 8, 2, 128, 800, [700, 333], 1, 0, "bf16"),        # chunk after a long context, ragged tiles
     (3, 64, 4, 1, 128, 256, [30, 64, 200], 1, 0, "bf16"),      # first rows of seq 0 see no key
     (3, 40, 4, 2, 64, 96, [0, 96, 500], 1, 0, "bf16"),         # empty cache; length past max_kv clamped
+    (2, 40, 4, 2, 64, 96, [-7, 50], 1, 0, "bf16"),             # negative length: an empty cache
     (2, 77, 8, 8, 128, 160, [150, 1], 0, 0, "bf16"),           # non-causal
     (2, 300, 8, 2, 128, 1100, [300, 1000], 1, 64, "bf16"),     # sliding window
     (1, 129, 4, 1, 64, 129, [129], 1, 1, "bf16"),              # window 1: own value

@@ -24,7 +24,12 @@ times rope_apply at an NTK-aware scaled base; `masked_prefill` times
 attn_prefill_masked (causal plus a key-padding mask) on LLaMA-7B-shaped heads.  `cpu_baseline` times the float64 oracle on a bounded sample on
 the host cores.
 
-    python bench.py [--steps K] [--warmup W] [--gpus 1] [--no-cpu-baseline] [--no-extras]
+Before the W warm-up steps the step runs untimed for --settle-s seconds
+(default 2): under sustained MFMA load the GPU lowers its clock within the
+first second or so, and a short run would otherwise be timed on that ramp.
+The settle time and step count are reported in `settle`.
+
+    python bench.py [--steps K] [--warmup W] [--settle-s S] [--gpus 1] [--no-cpu-baseline] [--no-extras]
 """
 import argparse
 import hashlib
@@ -234,6 +239,9 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=1000)
     ap.add_argument("--warmup", type=int, default=200)
+    ap.add_argument("--settle-s", type=float, default=2.0,
+                    help="seconds of untimed steps before the W warm-up steps, so the timed steps run at the "
+                         "clock the GPU holds under this load rather than on its ramp")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extras", action="store_true",
                     help="skip the prefill-extension and fused-RoPE timings after the steps "
@@ -303,10 +311,15 @@ def main():
     stream = torch.cuda.current_stream(dev)
     ev = lambda: torch.cuda.Event(enable_timing=True)
 
+    # Odd steps rotate by the negated positions, undoing the even step's
+    # rotation (up to bf16 rounding), so the timed Q/K stay the seeded draw
+    # rotated at most once instead of drifting over hundreds of rotations.
+    neg_pos = -torch.arange(wp.S, dtype=torch.int32, device=dev).repeat(wp.B, 1).contiguous()
+
     def step(i, rec=None):
         kc, vc = caches[i % 2]
         if rec: rec[0].record(stream)
-        R.rope_apply(q, k, None, wp.theta, wp.factor)
+        R.rope_apply(q, k, None if i % 2 == 0 else neg_pos, wp.theta, wp.factor)
         if rec: rec[1].record(stream)
         R.attn_prefill(q, k, v, out, causal=True, scale=wp.scale)
         if rec: rec[2].record(stream)
@@ -316,15 +329,23 @@ def main():
         R.attn_decode(dq.view(wd.B, wd.Hq, wd.D), kc, vc, lens_d, dout, scale=wd.scale, workspace=ws)
         if rec: rec[4].record(stream)
 
+    settle_steps, t0 = 0, time.perf_counter()
+    while time.perf_counter() - t0 < args.settle_s:
+        for _ in range(10):
+            step(settle_steps)
+            settle_steps += 1
+        torch.cuda.synchronize()
+    settle_s = time.perf_counter() - t0
     for i in range(args.warmup):
-        step(i)
+        step(settle_steps + i)
     torch.cuda.synchronize()
     recs = [[ev() for _ in range(5)] for _ in range(args.steps)]
     t_start, t_end = ev(), ev()
     torch.cuda.synchronize()
     t_start.record(stream)
+    first = settle_steps + args.warmup  # keeps the +/- rotation alternation
     for i in range(args.steps):
-        step(i, recs[i])
+        step(first + i, recs[i])
     t_end.record(stream)
     torch.cuda.synchronize()
     total_ms = t_start.elapsed_time(t_end)
@@ -347,6 +368,7 @@ def main():
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
+        "settle": {"seconds": round(settle_s, 2), "steps": settle_steps},
         "ms_per_step": round(total_ms / args.steps, 4),
         "higher_is_better": True,
         "scaling": "weak",

@@ -281,12 +281,14 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
   l_run += __shfl_xor(l_run, 16);
   l_run = half_swap_sum(l_run);
 
-  // combine the waves in LDS: [w][16 heads][D + 3] fp32 (m, l, acc[D], one
-  // pad: with an odd row stride the 64 lanes (head n, lane group g) of each
-  // store land on at most two per bank; the readers take consecutive columns)
+  // combine the waves in LDS: [w][16 heads][D + 2] fp32 (m, l, acc[D]).  The
+  // rows stay 8-byte aligned, so each lane's accumulator run goes out in
+  // 8-byte stores (an odd stride, tried to spread the banks, split them into
+  // 4-byte stores and measured more LDS instructions and more conflict
+  // cycles); the readers take consecutive columns.
   __syncthreads();
   float* st = reinterpret_cast<float*>(lds);
-  constexpr int SR = D + 3;
+  constexpr int SR = D + 2;
   static_assert(DW * 16 * SR * sizeof(float) <= sizeof(lds), "combine area");
   float* mine = st + (w * 16 + n) * SR;
   if (g == 0) {

@@ -95,6 +95,36 @@ def cpu_baseline(budget_s=12.0):
                       f"{len(os.sched_getaffinity(0))}"}
 
 
+def cpu_oracle_configs():
+    """Seconds of the float64 oracle on the small workloads (C1, C2a, C2b: whole,
+    RoPE included where the workload has it) and on the first 8 sequences of the
+    decode workload (rotation, append and decode), for the baseline table."""
+    import oracle
+    from rope_causal_gqa_amd import workloads as W
+    out = {}
+    for name in ("c1", "c2a", "c2b"):
+        w = W.WORKLOADS[name]
+        q, k, v = (W.to_f64(a, w.dtype) for a in W.prefill_inputs(w))
+        t0 = time.perf_counter()
+        if w.rope:
+            q, k = oracle.rope_apply(q, k, None, w.theta, w.factor)
+        oracle.attention(q, k, v, w.causal, w.scale)
+        out[name] = {"seconds": round(time.perf_counter() - t0, 4), "sample": "whole workload"}
+    w = W.WORKLOADS["c5"]
+    nb = 8
+    inp = W.decode_inputs(w, B=nb)
+    f = lambda a: W.to_f64(a, w.dtype)
+    t0 = time.perf_counter()
+    ctx = inp["ctx"]
+    oracle.rope_decode_step(f(inp["q"]), f(inp["k_new"]), f(inp["v_new"]), f(inp["k_cache"]), f(inp["v_cache"]),
+                            ctx + 1, None, w.scale, w.theta, w.factor)
+    dt = time.perf_counter() - t0
+    kv_bytes = float(np.sum(ctx.astype(np.int64) + 1)) * w.Hkv * w.D * 2 * 2
+    out["c5"] = {"seconds": round(dt, 4), "sample": f"first {nb} of {w.B} sequences",
+                 "gbps": round(kv_bytes / dt / 1e9, 3)}
+    return out
+
+
 def _time_launches(fn, stream, warmup=20, reps=200):
     """Mean time (ms) of one launch of fn, HIP events on the launch stream."""
     import torch
@@ -402,6 +432,7 @@ def main():
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()
+        res["cpu_oracle_configs"] = cpu_oracle_configs()
     print(json.dumps(res), flush=True)
 
 

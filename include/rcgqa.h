@@ -166,6 +166,48 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
                           rcgqa_dtype dt, rcgqa_stream stream);
 
 /*
+ * attn_prefill_workspace_bytes -- bytes of scratch attn_prefill_ws needs for
+ * these sizes.  Pure host function.  0 when the problem runs without one (it
+ * is large enough for one workgroup per query tile, or not causal); returns 0
+ * if an argument is not positive.
+ */
+size_t attn_prefill_workspace_bytes(int B, int S, int Hq, int head_dim, int causal);
+
+/*
+ * attn_prefill_ws -- attn_prefill with a caller-owned workspace, which lets
+ * small causal problems spread each query tile's keys over several
+ * workgroups.
+ *
+ * Defines: as attn_prefill ([HF] section 1.2 steps 2-4 and section 2 steps
+ * 4-5; repeat_kv head map).  For a causal bf16 problem too small to fill the
+ * GPU with one workgroup per 256-row query tile (for example one GPU's
+ * 8-query-head / 1-KV-head share of a 64-head layer, the head split of [L2X]
+ * section 3.1), the work is listed as (256-row query tile, 64-key tile)
+ * steps and cut into 256 contiguous ranges of equal cost, one per
+ * workgroup, which may cross query tiles (stream-K).  A query tile shared by
+ * several workgroups is finished by the last of them to end: each writes its
+ * softmax state (fp32 O, running max, row sum) to the workspace, and the
+ * last merges the states in key order, so the result is repeatable bit for
+ * bit.  Other problems (large, non-causal, fp32) run exactly as attn_prefill.
+ *
+ * Arguments as attn_prefill, plus:
+ * workspace  device buffer of at least attn_prefill_workspace_bytes(B, S, Hq,
+ *            head_dim, causal) bytes (may be null when that is 0), 256-byte
+ *            aligned, owned by the caller.  Its first 4096 bytes hold per-tile
+ *            counters and must be zero before its first use (for example
+ *            hipMemset of the whole buffer); every call leaves them zero, so
+ *            one workspace serves later calls of any shape it is large
+ *            enough for.  Concurrent calls must not share a workspace.
+ * Errors as attn_prefill; a workspace that is too small, misaligned or null
+ * when needed is RCGQA_EINVAL (nothing launched).
+ */
+rcgqa_status attn_prefill_ws(const void* q, const void* k, const void* v, void* out,
+                             int B, int S, int Hq, int Hkv, int head_dim,
+                             int causal, float scale, rcgqa_dtype dt,
+                             void* workspace, size_t workspace_bytes,
+                             rcgqa_stream stream);
+
+/*
  * attn_prefill_masked -- attn_prefill with a general additive mask.
  *
  * Defines: [HF] section 1.2 step 3 (the attention mask is sliced to the query

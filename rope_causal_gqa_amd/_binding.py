@@ -43,6 +43,10 @@ def lib():
     L.rope_apply_interleaved.restype = i32
     L.attn_prefill.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_prefill.restype = i32
+    L.attn_prefill_workspace_bytes.argtypes = [i32, i32, i32, i32, i32]
+    L.attn_prefill_workspace_bytes.restype = sz
+    L.attn_prefill_ws.argtypes = [vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
+    L.attn_prefill_ws.restype = i32
     L.attn_prefill_masked.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_prefill_masked.restype = i32
     L.attn_prefill_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
@@ -173,6 +177,37 @@ def attn_prefill(q, k, v, out=None, causal=True, *, scale):
                             _dev(out, "out", dt, 4), B, S, Hq, Hkv, D, int(bool(causal)),
                             float(scale), dt, _stream(q))
     _check(st, "attn_prefill")
+    return out
+
+
+def attn_prefill_workspace_bytes(B, S, Hq, head_dim, causal=True):
+    return int(lib().attn_prefill_workspace_bytes(B, S, Hq, head_dim, int(bool(causal))))
+
+
+def attn_prefill_ws(q, k, v, out=None, causal=True, *, scale, workspace=None):
+    """attn_prefill with a caller-owned workspace that lets small causal
+    problems split each query tile's keys over several workgroups (see rcgqa.h).
+    ``workspace`` (uint8, at least attn_prefill_workspace_bytes) must be zeroed
+    before its first use; every call leaves it ready for the next.  Without one
+    a zeroed buffer is allocated for this call."""
+    import torch
+    dt = _dtype_code(q)
+    B, S, Hq, D = q.shape
+    Hkv = k.shape[2]
+    if tuple(k.shape) != (B, S, Hkv, D) or tuple(v.shape) != (B, S, Hkv, D):
+        raise ValueError("k and v must be [B, S, Hkv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, S, Hq, D):
+        raise ValueError("out must be [B, S, Hq, D]")
+    if workspace is None:
+        need = attn_prefill_workspace_bytes(B, S, Hq, D, causal) if dt == BF16 else 0
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_prefill_ws(_dev(q, "q", dt, 4), _dev(k, "k", dt, 4), _dev(v, "v", dt, 4),
+                               _dev(out, "out", dt, 4), B, S, Hq, Hkv, D, int(bool(causal)), float(scale), dt,
+                               _dev(workspace, "workspace"), wbytes, _stream(q))
+    _check(st, "attn_prefill_ws")
     return out
 
 

@@ -142,6 +142,34 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
                                               Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
 }
 
+size_t attn_prefill_workspace_bytes(int B, int S, int Hq, int head_dim, int causal) {
+  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(head_dim)) return 0;
+  if (mul({B, Hq}) > kI32Max || !attn_head_dim(head_dim)) return 0;
+  return rcgqa::prefill_split_workspace_bytes(B, S, Hq, head_dim, causal != 0);
+}
+
+rcgqa_status attn_prefill_ws(const void* q, const void* k, const void* v, void* out, int B, int S, int Hq, int Hkv,
+                             int head_dim, int causal, float scale, rcgqa_dtype dt, void* workspace,
+                             size_t workspace_bytes, rcgqa_stream stream) {
+  if (!q || !k || !v || !out || !good_dtype(dt) || !al16({q, k, v, out})) return RCGQA_EINVAL;
+  if (out == q || out == k || out == v) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(S) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv) return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (mul({B, Hq}) > kI32Max || mul({B, S, Hq, head_dim}) < 0) return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || !prefill_grid_ok(B, Hq, S)) return RCGQA_EUNSUPPORTED;
+  const size_t need = dt == RCGQA_BF16 ? attn_prefill_workspace_bytes(B, S, Hq, head_dim, causal) : 0;
+  if (need && (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256))
+    return RCGQA_EINVAL;
+  if (workspace && (workspace == q || workspace == k || workspace == v || workspace == out)) return RCGQA_EINVAL;
+  const hipStream_t st = (hipStream_t)stream;
+  const rcgqa::KvSpec kv{(long long)S * Hkv * head_dim, head_dim, (long long)Hkv * head_dim, nullptr, S, 0};
+  if (dt == RCGQA_BF16)
+    return hip_status(rcgqa::launch_prefill_bf16_split(q, k, v, out, B, S, Hq, Hkv, head_dim, causal != 0, scale, kv,
+                                                       need ? workspace : nullptr, st));
+  return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k, (const float*)v, (float*)out, B, S,
+                                              Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
+}
+
 rcgqa_status attn_prefill_masked(const void* q, const void* k, const void* v, const void* mask, void* out, int B,
                                  int S, int Hq, int Hkv, int head_dim, int mask_heads, int mask_ld, int causal,
                                  float scale, rcgqa_dtype dt, rcgqa_stream stream) {

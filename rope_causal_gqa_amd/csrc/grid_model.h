@@ -85,5 +85,100 @@ inline KeyGroupGrid key_group_grid(long long bh, int Sq, bool causal, long long 
   return {four, four ? npairs2 : nqt4};
 }
 
+// Stream-K plan for small causal grids (no cache, no mask).  A unit is one
+// (query tile of BM rows, 64-key tile) step of the causal work.  Units are
+// listed (batch, head) by (batch, head); within one, query tiles in heavy /
+// light pairs (the last tile, the first, the second last, the second, ...),
+// and within a tile key tile by key tile.  Each workgroup takes a contiguous
+// range of the list.  The ranges balance a cost of one per unit plus
+// `tile_cost` per tile started (the prologue and the hand-over a piece of a
+// tile brings), through the cumulative cost C(u) = u + tile_cost * (tiles
+// that start before unit u): workgroup w starts at the first unit u with
+// C(u) G >= w C(units).  A query tile whose units fall to several
+// workgroups is finished by merging their partial softmax states; each
+// workgroup has at most two such pieces (the first and the last of its
+// range), kept in slots 2 w and 2 w + 1.  All in 32-bit integers (the plan
+// is used only where C(units) G fits), constexpr so that the kernel runs
+// this code: every (batch, head) block has the same layout, so each step is
+// one division and a walk over one block's tiles.
+constexpr int stream_ntiles(int Sq, int qt, int BM) {
+  return ((Sq < BM * (qt + 1) ? Sq : BM * (qt + 1)) + 63) / 64;
+}
+// query tile of list position j within a (batch, head) block
+constexpr int stream_pair_qt(int j, int nqt) { return (j & 1) ? (j >> 1) : nqt - 1 - (j >> 1); }
+
+struct StreamPlan {
+  int nqt;        // query tiles per (batch, head)
+  int per;        // units per (batch, head)
+  int units;      // all units
+  int G;          // workgroups
+  int tile_cost;  // cost of starting a tile, in units
+  int cost;       // C(units)
+  bool ok;        // the sizes fit the 32-bit arithmetic
+};
+
+inline StreamPlan stream_plan(long long bh, int Sq, int BM, int slots, int min_units, int tile_cost) {
+  const int nqt = (Sq + BM - 1) / BM;
+  long long per = 0;
+  for (int qt = 0; qt < nqt; qt++) per += stream_ntiles(Sq, qt, BM);
+  const long long units = bh * per, cost = units + (long long)tile_cost * bh * nqt;
+  // at least min_units units and more than tile_cost + 1 of cost per workgroup, so that no range is empty
+  const long long G =
+      std::max<long long>(1, std::min<long long>(slots, units / std::max(min_units, tile_cost + 2)));
+  const bool ok = cost * (G + 1) < (1LL << 31);
+  return {nqt, (int)per, (int)units, (int)G, tile_cost, (int)cost, ok};
+}
+
+// The query tile that unit u falls in: its (batch, head), query tile qt, key
+// tile k within it, its key-tile count n, its first unit t0, its counter
+// slot (bh nqt + qt) and the number of tiles that start before it.
+struct StreamTile {
+  int bh, qt, k, n, t0, tile, before;
+};
+constexpr StreamTile stream_tile(int u, int nqt, int per, int Sq, int BM) {
+  const int b = u / per, r = u - b * per;
+  int s = 0, j = 0;
+  for (; j < nqt - 1; j++) {
+    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM);
+    if (r < s + n) break;
+    s += n;
+  }
+  const int qt = stream_pair_qt(j, nqt);
+  return {b, qt, r - s, stream_ntiles(Sq, qt, BM), b * per + s, b * nqt + qt, b * nqt + j};
+}
+
+// C(u) for 0 <= u <= units
+constexpr int stream_cost(int u, int units, int nqt, int per, int Sq, int BM, int tile_cost) {
+  if (u >= units) return units + tile_cost * (units / per) * nqt;
+  const StreamTile t = stream_tile(u, nqt, per, Sq, BM);
+  return u + tile_cost * (t.before + (u > t.t0 ? 1 : 0));
+}
+
+// First unit of workgroup w (w = G gives `units`): the first u with
+// C(u) >= c = ceil(w cost / G), found in the (batch, head) block that c
+// falls in (each block adds per + tile_cost nqt to C)
+constexpr int stream_start(int w, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost) {
+  const int c = (w * cost + G - 1) / G;
+  const int cb = per + tile_cost * nqt;
+  const int b = c / cb, rem = c - b * cb;
+  if (b * per >= units) return units;
+  int s = 0;
+  for (int j = 0; j < nqt; j++) {
+    if (rem <= s + tile_cost * j) return b * per + s;  // at tile j's first unit
+    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM);
+    if (rem <= s + n + tile_cost * (j + 1)) {           // inside tile j: C = u + tile_cost (j + 1)
+      const int r = rem - tile_cost * (j + 1);
+      return b * per + (r > s + 1 ? r : s + 1);
+    }
+    s += n;
+  }
+  return b * per + per;
+}
+
+// Workgroup that runs unit u (u < units)
+constexpr int stream_owner(int u, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost) {
+  return stream_cost(u, units, nqt, per, Sq, BM, tile_cost) * G / cost;
+}
+
 }  // namespace grid
 }  // namespace rcgqa

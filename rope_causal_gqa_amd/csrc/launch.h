@@ -51,6 +51,20 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
                                int Hq, int Hkv, int D, bool causal, float scale, const KvSpec& kv,
                                const float* q_rope, hipStream_t st);
 
+// Stream-K prefill for small causal grids without a cache or a mask (see
+// grid::stream_plan): each workgroup runs an equal-cost range of (query
+// tile, key tile) steps; pieces of a query tile shared by several
+// workgroups write fp32 partial states to `ws` and the last one merges them.
+// prefill_split_workspace_bytes is what `ws` must hold for these sizes (0 when
+// the problem takes the one-workgroup-per-tile grids).  Its first 4 KB hold
+// the per-tile counters of every shape: they must be zero before the first
+// call, and every call leaves them zero.  Falls back to launch_prefill_bf16
+// when the split is not used.
+size_t prefill_split_workspace_bytes(int B, int Sq, int Hq, int D, bool causal);
+hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
+                                     int Hkv, int D, bool causal, float scale, const KvSpec& kv, void* ws,
+                                     hipStream_t st);
+
 // Split-K decode: partial softmax states go to `ws`, then a merge pass writes out.
 size_t decode_workspace_bytes(int B, int Hq, int D, int max_kv);
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* kv_lens, void* out,

@@ -91,6 +91,24 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
                "s"(m));
 }
 
+// Stream-K state of one launch (SPL kernels only; see grid::stream_plan):
+// one counter per query tile at cnt, partial O blocks of BM x D floats at o
+// (each in the accumulator layout: [wave][register][lane]), the (reference
+// max, row sum) pairs [slot][BM][2] of their rows at ml; the plan's units
+// per (batch, head), total cost and cost per tile start; the first unit of
+// every query tile of a (batch, head) block in list order (tstart[nqt] =
+// per) and of every workgroup (wstart[G] = all units), computed on the host.
+constexpr int kStreamMaxTiles = 64;   // query tiles per (batch, head)
+constexpr int kStreamMaxGroups = 256;
+struct SplitArgs {
+  float* o;
+  float* ml;
+  int* cnt;
+  int per, cost, tile_cost;
+  int tstart[kStreamMaxTiles + 1];
+  int wstart[kStreamMaxGroups + 1];
+};
+
 // GEN: keys through per-sequence counts (query rows aligned to the end of
 // their sequence) and an optional sliding window; without it every sequence
 // has Sq keys, queries and keys aligned, and the bounds fold to constants.
@@ -102,12 +120,18 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
 // buffers fit in LDS.
 // MSK: an additive mask (kv.mask, plain layout) is added to the scores; each
 // lane loads its row's values for the next tile while the current one runs.
-template <int D, int NW, bool GEN, int KSPLIT, int BNT, bool MSK>
+// SPL: stream-K over workgroups (causal, no cache or mask): workgroup w runs
+// a range of units of the causal work (grid::stream_plan), which may cross
+// query tiles; a piece of a tile that other workgroups share writes its
+// (O, m_ref, l) rows to the split workspace, and the workgroup that completes
+// the tile's count merges the pieces in key order and writes the rows (no
+// workgroup ever waits for another).
+template <int D, int NW, bool GEN, int KSPLIT, int BNT, bool MSK, bool SPL = false>
 __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __restrict__ q, const bf16* __restrict__ k,
                                                              const bf16* __restrict__ v, bf16* __restrict__ out,
                                                              int Sq, int Hq, int Hkv, int causal, float c_log2,
                                                              int nqt, int npairs, KvSpec kv,
-                                                             const float* __restrict__ q_rope) {
+                                                             const float* __restrict__ q_rope, SplitArgs sp) {
   constexpr int BN = BNT;           // keys per K/V tile
   constexpr int NKB = BN / 32;      // 32-key blocks per tile
   constexpr int NWG = NW / KSPLIT;  // waves per key group
@@ -126,6 +150,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   constexpr bool MSTAGE = MSK && NW == 8 && KSPLIT == 1;
   constexpr int MTILE = MSTAGE ? 32 * NW * BN : 0;
   __shared__ __attribute__((aligned(16))) bf16 lds[KSPLIT * 2 * 2 * TILE + 2 * MTILE];  // [group][buffer][K | V][BN][D]
+  __shared__ int split_last;  // SPL: this workgroup completed its tile's count
 
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int wu = __builtin_amdgcn_readfirstlane(w);
@@ -140,23 +165,24 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   // hit its L2.  A slot is either one query tile or, when there are enough
   // workgroups to fill the GPU (npairs < nqt), the pair (nqt-1-p, p): a
   // heavy and a light causal tile, so every workgroup does the same work.
+  // (Stream-K workgroups take contiguous unit ranges per XCD the same way.)
   const int total = (int)gridDim.x;
   const int wid = (int)blockIdx.x;
   const int item = (total & 7) == 0 ? (wid & 7) * (total >> 3) + (wid >> 3) : wid;
-  const int bh = item / npairs, slot = item - bh * npairs;
+  const size_t qrs = (size_t)Hq * D, kvrs = (size_t)kv.sr;
+  // One query tile of (batch, head) bh at rows [q0, q0 + BM).  SPL: key tiles
+  // [seg_lo, seg_hi) of the tile, which starts at unit seg_t0, has counter
+  // seg_tile and seg_before tiles before it in the list; this workgroup's
+  // range starts at unit seg_a.
+  auto run_qtile = [&](const int q0, const int bh, const int seg_lo, const int seg_hi, const int seg_t0,
+                       const int seg_tile, const int seg_before, const int seg_a) __attribute__((always_inline)) {
   const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / (Hq / Hkv);
-  const size_t qrs = (size_t)Hq * D, kvrs = (size_t)kv.sr;
   const bf16* kb = k + (size_t)b * kv.sb + (size_t)kvh * kv.sh;
   const bf16* vb = v + (size_t)b * kv.sb + (size_t)kvh * kv.sh;
   // this sequence's keys; query i sits at absolute position i + off
   const int nkeys = GEN ? min(max(kv.lens[b], 0), kv.max_kv) : Sq;
   const int off = GEN ? nkeys - Sq : 0, W = GEN ? kv.window : 0;
-  // heavy (late) causal query tiles first: with more workgroups than fit at
-  // once, the light ones then fill in behind them
-  const int qt_first = (npairs < nqt || causal) ? nqt - 1 - slot : slot;
-  const int npass = (npairs < nqt && slot != nqt - 1 - slot) ? 2 : 1;
-  auto run_qtile = [&](const int q0) __attribute__((always_inline)) {
 
   const int qrow = q0 + wr * 32 + col;  // this lane's query row
   bf16x8 qf[KS];
@@ -297,9 +323,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int key_hi = causal ? min(nkeys, q0 + BM + off) : nkeys;
   const int key_lo = (causal && W > 0) ? max(0, q0 + off - W + 1) : 0;
   const int t_lo = key_lo / BN, t_hi = key_hi > 0 ? (key_hi + BN - 1) / BN : 0;
-  // this group's tiles [tg_lo, tg_hi) (possibly empty); all groups run `steps` barrier steps
-  const int ntl = max(t_hi - t_lo, 0), steps = (ntl + KSPLIT - 1) / KSPLIT;
-  const int tg_lo = t_lo + grp * steps, tg_hi = min(tg_lo + steps, t_lo + ntl);
+  // this group's tiles [tg_lo, tg_hi) (possibly empty); all groups run `steps` barrier steps.
+  // A stream-K piece takes the tiles [seg_lo, seg_hi) of its range (t_lo = 0 there).
+  const int ntl = max(t_hi - t_lo, 0);
+  const int steps = SPL ? seg_hi - seg_lo : (ntl + KSPLIT - 1) / KSPLIT;
+  const int tg_lo = SPL ? seg_lo : t_lo + grp * steps;
+  const int tg_hi = SPL ? seg_hi : min(tg_lo + steps, t_lo + ntl);
   const int wrow_lo = q0 + wr * 32, wrow_hi = wrow_lo + 31;
 
   // transpose-read addressing of V (fixed per lane)
@@ -551,7 +580,95 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     __syncthreads();  // the hand-over area is free again before any later tile load
   }
 
-  const float l_tot = half_swap_sum(l_run);
+  float l_tot = half_swap_sum(l_run);
+  if constexpr (SPL) {
+    // workgroups [w0, w1] share this tile; a piece of a shared tile hands its
+    // state over (this workgroup's logical index is `item`, its first unit seg_a)
+    // owner of unit u: C(u) G / cost, with C(u) = u + tile_cost (tiles started before u)
+    const int G = total;
+    const int w0 = (seg_t0 + sp.tile_cost * seg_before) * G / sp.cost;
+    const int w1 = (seg_t0 + ntl - 1 + sp.tile_cost * (seg_before + (ntl > 1 ? 1 : 0))) * G / sp.cost;
+    if (w1 > w0) {
+      // The pieces run on any XCD, and each XCD has its own L2, so the
+      // hand-over goes through memory without whole-cache maintenance (an L2
+      // write-back and invalidate per workgroup measured 4x slower): the
+      // state is stored with system-scope stores (written through the L2),
+      // this wave waits until they are acknowledged, and only then does the
+      // workgroup count itself in with a system-scope atomic.  The workgroup
+      // that brings the count to the number of pieces reads the others'
+      // states with system-scope loads (served from memory, not from a stale
+      // L2 line) issued after it has seen the count, so it sees every store.
+      // O goes in the accumulators' own layout, register-major ([wave]
+      // [register][lane]), so each store writes 256 contiguous bytes and the
+      // merge reads it back into the same waves and lanes.
+      const int r = wr * 32 + col;
+      // slot 2 w for a workgroup's first piece, 2 w + 1 for its last
+      const long long me = 2LL * item + (seg_t0 > seg_a ? 1 : 0);
+      const float m_me = lim > -1e29f ? m_ref : -1e30f;  // -1e30: no key seen, weight 0 in the merge
+      const size_t wl = (size_t)wr * (DB * 16) * 64 + lane;
+      float* po = sp.o + (size_t)me * BM * D + wl;
+#pragma unroll
+      for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int i = 0; i < 16; i++)
+          __hip_atomic_store(po + (db * 16 + i) * 64, o[db][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      if (hf == 0) {
+        float* pm = sp.ml + ((size_t)me * BM + r) * 2;
+        __hip_atomic_store(pm, m_me, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(pm + 1, l_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      }
+      __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (expcnt, lgkmcnt not waited on): stores acknowledged
+      __syncthreads();
+      int* const cnt = sp.cnt + seg_tile;
+      if (tid == 0)
+        split_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == (int)(w1 - w0);
+      __syncthreads();
+      if (!split_last) return;
+      auto ld = [](const float* p) __attribute__((always_inline)) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      };
+      // merge in workgroup order (= key order), this piece from registers:
+      // the same arithmetic in the same order whichever workgroup merges
+      // the tile starts inside workgroup w0's range (its last piece) or at its
+      // first unit; for every later workgroup it is the first piece
+      const long long s0 = 2LL * w0 + (seg_t0 > sp.wstart[w0] ? 1 : 0);
+      auto slot_of = [&](int ww) __attribute__((always_inline)) { return ww == w0 ? s0 : 2LL * ww; };
+      float M = -1e30f;
+      for (int ww = w0; ww <= w1; ww++) {
+        const long long sl = slot_of(ww);
+        M = fmaxf(M, sl == me ? m_me : ld(sp.ml + ((size_t)sl * BM + r) * 2));
+      }
+      f32x16 acc[DB];
+#pragma unroll
+      for (int db = 0; db < DB; db++) acc[db] = f32x16{};
+      float den = 0.f;
+      for (int ww = w0; ww <= w1; ww++) {
+        const long long sl = slot_of(ww);
+        if (sl == me) {
+          const float e = m_me > -1e29f ? fast_exp2(m_me - M) : 0.f;
+          den = fmaf(e, l_tot, den);
+#pragma unroll
+          for (int db = 0; db < DB; db++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[db][i] = fmaf(e, o[db][i], acc[db][i]);
+        } else {
+          const float* pm = sp.ml + ((size_t)sl * BM + r) * 2;
+          const float mc = ld(pm), lc = ld(pm + 1);
+          const float e = mc > -1e29f ? fast_exp2(mc - M) : 0.f;
+          den = fmaf(e, lc, den);
+          const float* pc = sp.o + (size_t)sl * BM * D + wl;
+#pragma unroll
+          for (int db = 0; db < DB; db++)
+#pragma unroll
+            for (int i = 0; i < 16; i++) acc[db][i] = fmaf(e, ld(pc + (db * 16 + i) * 64), acc[db][i]);
+        }
+      }
+#pragma unroll
+      for (int db = 0; db < DB; db++) o[db] = acc[db];
+      l_tot = den;
+      if (tid == 0) __hip_atomic_store(cnt, 0, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);  // zero for the next call
+    }
+  }
   const float inv = l_tot > 0.f ? 1.f / l_tot : 0.f;
   if (grp == 0 && qrow < Sq) {
     bf16* dst = out + ((size_t)b * Sq + qrow) * qrs + (size_t)h * D;
@@ -568,8 +685,32 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     }
   }
   };  // run_qtile
-  run_qtile(qt_first * BM);
-  if (npass == 2) run_qtile(slot * BM);
+  if constexpr (SPL) {
+    // this workgroup's units, piece by piece
+    const int u_a = sp.wstart[item], u_end = sp.wstart[item + 1];
+    for (int u = u_a; u < u_end;) {
+      // the tile unit u falls in: (batch, head) block, then the last tile start <= u in the block
+      const int b_ = u / sp.per, r = u - b_ * sp.per;
+      int lo = 0, hi = nqt - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi + 1) >> 1;
+        if (sp.tstart[mid] <= r) lo = mid;
+        else hi = mid - 1;
+      }
+      const int qt = grid::stream_pair_qt(lo, nqt);
+      const int t0 = b_ * sp.per + sp.tstart[lo], n = sp.tstart[lo + 1] - sp.tstart[lo], k0 = r - sp.tstart[lo];
+      const int k_hi = min(n, k0 + (u_end - u));
+      run_qtile(qt * BM, b_, k0, k_hi, t0, b_ * nqt + qt, b_ * nqt + lo, u_a);
+      u += k_hi - k0;
+    }
+  } else {
+    const int bh = item / npairs, slot = item - bh * npairs;
+    // heavy (late) causal query tiles first: with more workgroups than fit at
+    // once, the light ones then fill in behind them
+    const int qt_first = (npairs < nqt || causal) ? nqt - 1 - slot : slot;
+    run_qtile(qt_first * BM, bh, 0, 0, 0, 0, 0, 0);
+    if (npairs < nqt && slot != nqt - 1 - slot) run_qtile(slot * BM, bh, 0, 0, 0, 0, 0, 0);
+  }
 }
 
 template <int NW, bool GEN, int KSPLIT, int BNT>
@@ -584,7 +725,7 @@ static void launch_nw(const void* q, const void* k, const void* v, void* out, in
 #define RCGQA_PREFILL_LAUNCH(DD, M)                                                                               \
   hipLaunchKernelGGL((prefill_bf16_kernel<DD, NW, GEN, KSPLIT, BNT, M>), grid, block, 0, st, (const bf16*)q,    \
                      (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, (int)causal, c_log2, nqt, npairs, kv, \
-                     q_rope)
+                     q_rope, SplitArgs{})
   if (D == 64) {
     if (msk) RCGQA_PREFILL_LAUNCH(64, !GEN);
     else RCGQA_PREFILL_LAUNCH(64, false);
@@ -603,6 +744,78 @@ static void launch_nw(const void* q, const void* k, const void* v, void* out, in
     launch_nw<NW, true, KSPLIT, BNT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
   else
     launch_nw<NW, false, KSPLIT, BNT>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, npairs, kv, q_rope, st);
+}
+
+namespace {
+// Whether the launcher would take the key-group grids (one 8-wave workgroup
+// per CU) for this problem: the split-K path replaces them for causal
+// prefills without a cache or a mask.
+bool small_grid(long long bh, int Sq, bool causal, const KvSpec& kv) {
+  const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
+  const bool short_window = kv.window > 0 && kv.window < 2048;
+  const bool mask_ok = !kv.mask || (kv.msr % 8 == 0 && kv.msr >= 8);
+  if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512 && !short_window && mask_ok) return false;
+  const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;
+  return bh * (pair4 ? (nqt4 + 1) / 2 : nqt4) < 512;
+}
+// The split workspace starts with a fixed block of per-tile counters, so that
+// calls of any shape find theirs at the same place (zeroed by the last call);
+// the partial states follow it, two slots per workgroup.
+constexpr int kSplitCounters = 1024;
+constexpr size_t kSplitCounterBytes = kSplitCounters * sizeof(int);
+constexpr int kStreamBM = 256;     // 8-wave workgroups, one per CU
+constexpr int kStreamMinUnits = 4;  // units per workgroup at least
+constexpr int kStreamTileCost = 2;  // cost of a tile start, in units (its prologue; best of 0-6 measured)
+bool split_applies(long long bh, int Sq, bool causal, const KvSpec& kv) {
+  return causal && !kv.lens && kv.window <= 0 && !kv.mask && small_grid(bh, Sq, causal, kv) &&
+         bh * ((Sq + kStreamBM - 1) / kStreamBM) <= kSplitCounters && (Sq + kStreamBM - 1) / kStreamBM <= kStreamMaxTiles &&
+         grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost).ok;
+}
+grid::StreamPlan stream_plan_for(long long bh, int Sq) {
+  return grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost);
+}
+}  // namespace
+
+size_t prefill_split_workspace_bytes(int B, int Sq, int Hq, int D, bool causal) {
+  const long long bh = (long long)B * Hq;
+  const KvSpec kv{};
+  if (!split_applies(bh, Sq, causal, kv)) return 0;
+  const grid::StreamPlan p = stream_plan_for(bh, Sq);
+  return kSplitCounterBytes + sizeof(float) * 2 * (size_t)p.G * kStreamBM * (size_t)(D + 2);
+}
+
+hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
+                                     int Hkv, int D, bool causal, float scale, const KvSpec& kv, void* ws,
+                                     hipStream_t st) {
+  const long long bh = (long long)B * Hq;
+  if (!ws || !split_applies(bh, Sq, causal, kv))
+    return launch_prefill_bf16(q, k, v, out, B, Sq, Hq, Hkv, D, causal, scale, kv, nullptr, st);
+  const float c_log2 = (float)((double)scale * 1.4426950408889634);
+  const grid::StreamPlan p = stream_plan_for(bh, Sq);
+  const size_t nslots = 2 * (size_t)p.G;
+  SplitArgs sa;
+  sa.cnt = reinterpret_cast<int*>(ws);
+  sa.o = reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCounterBytes);
+  sa.ml = sa.o + nslots * kStreamBM * D;
+  sa.per = p.per;
+  sa.cost = p.cost;
+  sa.tile_cost = p.tile_cost;
+  for (int j = 0, s = 0; j <= p.nqt; j++) {
+    sa.tstart[j] = s;
+    if (j < p.nqt) s += grid::stream_ntiles(Sq, grid::stream_pair_qt(j, p.nqt), kStreamBM);
+  }
+  for (int w = 0; w <= p.G; w++)
+    sa.wstart[w] = grid::stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, kStreamBM, p.tile_cost);
+  const dim3 grid((unsigned)p.G), block(512);
+  if (D == 64)
+    hipLaunchKernelGGL((prefill_bf16_kernel<64, 8, false, 1, 64, false, true>), grid, block, 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, 1, c_log2, p.nqt, p.nqt, kv, nullptr,
+                       sa);
+  else
+    hipLaunchKernelGGL((prefill_bf16_kernel<128, 8, false, 1, 64, false, true>), grid, block, 0, st, (const bf16*)q,
+                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, 1, c_log2, p.nqt, p.nqt, kv, nullptr,
+                       sa);
+  return hipGetLastError();
 }
 
 namespace {

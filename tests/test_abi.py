@@ -219,6 +219,7 @@ WS = ctypes.c_void_p(4096 * 64)
     lambda L: L.attn_prefill(A[0], A[1], MIS, A[3], 1, 4, 8, 2, 64, 1, 0.125, 0, None),
     lambda L: L.attn_prefill_cache(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 16, 1, 0, 0.125, 0, None),
     lambda L: L.attn_prefill_masked(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 1, 4, 1, 0.125, 0, None),
+    lambda L: L.attn_prefill_ws(A[0], MIS, A[2], A[3], 1, 4, 8, 2, 64, 1, 0.125, 0, WS, 1 << 20, None),
     lambda L: L.attn_decode(A[0], MIS, A[2], A[3], A[4], 1, 8, 2, 128, 16, 0.1, 0, WS, 1 << 30, None),
     lambda L: L.rope_attn_prefill(A[0], A[1], A[2], MIS, None, 1, 16, 8, 2, 64, 1, 0.125, 1e4, 1.0, 0, WS, 1 << 20,
                                   None),
@@ -239,6 +240,40 @@ def test_binding_requires_device_tensors():
         R.attn_prefill(q, q, q, scale=0.125)
     with pytest.raises(ValueError):
         R.attn_prefill_cache(q, q, q, torch.zeros(1, dtype=torch.int32), scale=0.125)
+
+
+def test_prefill_workspace_bytes():
+    L = R.lib()
+    # one GPU's 8-query-head share at 4096 tokens: stream-K over 256 workgroups,
+    # 4 KB of counters, then two partial states of 256 rows x (D + 2) floats per workgroup
+    n = L.attn_prefill_workspace_bytes(1, 4096, 8, 128, 1)
+    assert n == 4096 + 256 * 2 * 256 * 130 * 4
+    assert L.attn_prefill_workspace_bytes(1, 4096, 8, 64, 1) < n
+    assert L.attn_prefill_workspace_bytes(1, 4096, 8, 128, 0) == 0     # non-causal: no split
+    assert L.attn_prefill_workspace_bytes(2, 4096, 64, 128, 1) == 0    # fills the GPU without one
+    assert L.attn_prefill_workspace_bytes(0, 4096, 8, 128, 1) == 0
+    assert L.attn_prefill_workspace_bytes(1, 4096, 8, 96, 1) == 0
+
+
+@pytest.mark.parametrize("args", [
+    dict(ws=None), dict(wbytes=100), dict(ws_addr=4096 * 64 + 64), dict(ws_is_out=True), dict(out_is_q=True),
+    dict(Hq=6, Hkv=4), dict(causal=2), dict(scale=0.0), dict(D=9), dict(dt=3),
+])
+def test_prefill_ws_rejects(args):
+    a = dict(B=1, S=4096, Hq=8, Hkv=1, D=128, causal=1, scale=0.125, dt=0, ws_addr=4096 * 64, wbytes=1 << 30)
+    a.update(args)
+    q, k, v, out = A[0], A[1], A[2], A[3]
+    if args.get("out_is_q"):
+        out = q
+    ws = None if "ws" in args else (out if args.get("ws_is_out") else ctypes.c_void_p(a["ws_addr"]))
+    st = R.lib().attn_prefill_ws(q, k, v, out, a["B"], a["S"], a["Hq"], a["Hkv"], a["D"], a["causal"], a["scale"],
+                                 a["dt"], ws, a["wbytes"], None)
+    assert st == BD.EINVAL
+
+
+def test_prefill_ws_unsupported_head_dim():
+    assert R.lib().attn_prefill_ws(A[0], A[1], A[2], A[3], 1, 64, 8, 1, 96, 1, 0.1, 0, WS, 1 << 20, None) \
+        == BD.EUNSUPPORTED
 
 
 def test_fused_workspace_bytes():

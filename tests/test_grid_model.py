@@ -7,6 +7,7 @@ import random
 import shutil
 import subprocess
 
+import numpy as np
 import pytest
 
 CSRC = os.path.join(os.path.dirname(os.path.dirname(os.path.abspath(__file__))), "rope_causal_gqa_amd", "csrc")
@@ -29,6 +30,27 @@ int main() {
       std::vector<double> w(k);
       for (auto& x : w) std::scanf("%lf", &x);
       std::printf("%.3f\n", busiest_cu(w, bh));
+    } else if (what[0] == 's') {                // stream bh Sq BM min_units tile_cost: plan, then every piece
+      long long bh; int Sq, BM, mu, tc;
+      std::scanf("%lld %d %d %d %d", &bh, &Sq, &BM, &mu, &tc);
+      const StreamPlan p = stream_plan(bh, Sq, BM, kCUs, mu, tc);
+      std::printf("%d %d %d %d %d\n", p.nqt, p.units, p.G, p.cost, p.ok ? 1 : 0);
+      for (int w = 0; w < p.G; w++) {   // the kernel's walk over its range
+        const int a = stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
+        const int e = stream_start(w + 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
+        for (int u = a; u < e;) {
+          const StreamTile t = stream_tile(u, p.nqt, p.per, Sq, BM);
+          const int k_hi = std::min(t.n, t.k + (e - u));
+          const int w0 = stream_owner(t.t0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
+          const int w1 = stream_owner(t.t0 + t.n - 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
+          const long long me = 2LL * w + (t.t0 > a ? 1 : 0);
+          const long long s0 =
+              2LL * w0 + (t.t0 > stream_start(w0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc) ? 1 : 0);
+          std::printf("%d %d %d %d %d %d %d %d %lld %d %d %lld %d %d\n", w, t.bh, t.qt, t.k, k_hi, t.n, t.t0,
+                      t.tile, w1 > w0 ? me : -1LL, w0, w1, s0, a, e);
+          u += k_hi - t.k;
+        }
+      }
     } else {                                    // grid bh Sq causal nk window
       long long bh, nk; int Sq, causal, window;
       std::scanf("%lld %d %d %lld %d", &bh, &Sq, &causal, &nk, &window);
@@ -118,3 +140,90 @@ def test_grid_choice_on_timed_shapes(model, shape, four):
     nqt2, nqt4 = (Sq + 63) // 64, (Sq + 127) // 128
     paired = causal and nqt2 > 1 and bh * ((nqt2 + 1) // 2) >= 256
     assert int(got[1]) == (((nqt2 + 1) // 2 if paired else nqt2) if four else nqt4)
+
+
+@pytest.mark.parametrize("bh,Sq,BM,mu,tc", [(8, 4096, 256, 4, 3), (8, 2100, 256, 4, 3), (1, 1, 256, 4, 3),
+                                             (1, 257, 256, 4, 3), (4, 8192, 256, 4, 3), (16, 300, 256, 4, 3),
+                                             (2, 64, 256, 1, 0), (8, 1024, 128, 4, 2), (3, 5000, 256, 7, 5),
+                                             (64, 4096, 256, 4, 3)])
+def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc):
+    """The stream-K grid (small causal problems): workgroups take contiguous,
+    non-empty ranges of the unit list (batch-head, then query tiles in heavy /
+    light pairs, then key tile) that balance units plus tc per tile started;
+    the pieces cover every key tile a query tile sees under the causal rule
+    exactly once; a tile shared by several workgroups gives each of them a
+    distinct partial slot (at most two per workgroup, the first piece of a
+    range in slot 2w, the last in 2w + 1), and the merge order (workgroups
+    w0..w1, slot s0 for w0 and 2w after) is the key order."""
+    out = model([f"s {bh} {Sq} {BM} {mu} {tc}"])
+    nqt, units, G, cost, ok = (int(x) for x in out[0].split())
+    assert ok == (cost * (G + 1) < 2 ** 31) and ok
+    rows = [tuple(int(x) for x in r.split()) for r in out[1:]]
+    ntiles = [(min(Sq, BM * (qt + 1)) + 63) // 64 for qt in range(nqt)]
+    assert nqt == -(-Sq // BM) and units == bh * sum(ntiles) and cost == units + tc * bh * nqt
+    assert G == max(1, min(256, units // max(mu, tc + 2)))
+    # list order: (batch, head), then query tiles in heavy / light pairs
+    pairs = []
+    for p in range((nqt + 1) // 2):
+        pairs.append(nqt - 1 - p)
+        if p != nqt - 1 - p:
+            pairs.append(p)
+    assert sorted(pairs) == list(range(nqt))
+    order = [(b, qt) for b in range(bh) for qt in pairs]
+    t0 = {}
+    acc = 0
+    starts = []
+    for b, qt in order:
+        t0[(b, qt)] = acc
+        starts.append(acc)
+        acc += ntiles[qt]
+    # cost of every unit boundary, counted directly: C(u) = u + tc * (tiles starting before u)
+    started = np.zeros(units + 1, dtype=np.int64)
+    for x in starts:
+        started[x + 1:] += 1
+    Cu = np.arange(units + 1, dtype=np.int64) + tc * started
+
+    def C(u):
+        return int(Cu[u])
+    bounds = {}
+    cover = {}
+    slots = {}
+    per_wg = {}
+    for w, b, qt, klo, khi, n, t, tile, me, w0, w1, s0, a, e in rows:
+        bounds[w] = (a, e)
+        assert 0 <= b < bh and 0 <= qt < nqt and n == ntiles[qt]
+        assert t == t0[(b, qt)] and tile == b * nqt + qt
+        assert 0 <= klo < khi <= n and a <= t + klo and t + khi <= e
+        per_wg[w] = per_wg.get(w, 0) + khi - klo
+        cover.setdefault((b, qt), []).append((klo, khi, w, me, w0, w1, s0))
+        if w1 > w0:
+            assert 0 <= me < 2 * G and me // 2 == w and me not in slots
+            assert me == 2 * w + (1 if t > a else 0)
+            slots[me] = (b, qt)
+        else:
+            assert me == -1 and (klo, khi) == (0, n)
+    # ranges: contiguous, non-empty, each the brute-force first unit with C(u) G >= w cost
+    assert sorted(bounds) == list(range(G))
+    for w in range(G):
+        a, e = bounds[w]
+        assert a < e and per_wg[w] == e - a
+        assert a == int(np.nonzero(Cu * G >= w * cost)[0][0])
+        if w + 1 < G:
+            assert bounds[w + 1][0] == e
+    assert bounds[0][0] == 0 and bounds[G - 1][1] == units
+    assert len(cover) == bh * nqt
+    for (b, qt), pieces in cover.items():
+        pieces.sort()
+        assert pieces[0][0] == 0 and pieces[-1][1] == ntiles[qt]
+        assert all(pieces[i][1] == pieces[i + 1][0] for i in range(len(pieces) - 1))
+        ws = [p[2] for p in pieces]
+        w0, w1 = pieces[0][4], pieces[0][5]
+        assert ws == list(range(w0, w1 + 1))          # one piece per workgroup w0..w1, in key order
+        if w1 > w0:
+            s0 = pieces[0][6]
+            merge_slots = [s0] + [2 * w for w in range(w0 + 1, w1 + 1)]
+            assert merge_slots == [p[3] for p in pieces]
+    # balance: no range costs more than the mean plus one tile start and one unit
+    for w in range(G):
+        a, e = bounds[w]
+        assert C(e) - C(a) <= cost / G + tc + 1

@@ -92,16 +92,17 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
 }
 
 // Stream-K state of one launch (SPL kernels only; see grid::stream_plan):
-// one counter per query tile at cnt, partial O blocks of BM x D floats at o
-// (each in the accumulator layout: [wave][register][lane]), the (reference
-// max, row sum) pairs [slot][BM][2] of their rows at ml; the plan's units
+// one counter per query tile at cnt, partial O blocks of BM x D fp16 values
+// at o (pairs packed in 32-bit words, in the accumulator layout: [wave]
+// [register pair][lane]), the (reference max, row sum, O scale, unused)
+// rows [slot][BM][4] at ml; the plan's units
 // per (batch, head), total cost and cost per tile start; the first unit of
 // every query tile of a (batch, head) block in list order (tstart[nqt] =
 // per) and of every workgroup (wstart[G] = all units), computed on the host.
 constexpr int kStreamMaxTiles = 64;   // query tiles per (batch, head)
 constexpr int kStreamMaxGroups = 256;
 struct SplitArgs {
-  float* o;
+  uint32_t* o;
   float* ml;
   int* cnt;
   int per, cost, tile_cost;
@@ -598,24 +599,42 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       // that brings the count to the number of pieces reads the others'
       // states with system-scope loads (served from memory, not from a stale
       // L2 line) issued after it has seen the count, so it sees every store.
-      // O goes in the accumulators' own layout, register-major ([wave]
-      // [register][lane]), so each store writes 256 contiguous bytes and the
-      // merge reads it back into the same waves and lanes.
+      // A row's O goes as fp16 values scaled by the row's largest |O| (so in
+      // [-1, 1]; the scale travels in fp32 with m and l), in the accumulators'
+      // own layout, register-pair-major ([wave][register pair][lane]), so each
+      // store writes 256 contiguous bytes and the merge reads it back into
+      // the same waves and lanes.  The merge takes every piece, its own
+      // included, in this rounded form and in key order, so the result does
+      // not depend on which workgroup merges.
       const int r = wr * 32 + col;
       // slot 2 w for a workgroup's first piece, 2 w + 1 for its last
       const long long me = 2LL * item + (seg_t0 > seg_a ? 1 : 0);
       const float m_me = lim > -1e29f ? m_ref : -1e30f;  // -1e30: no key seen, weight 0 in the merge
-      const size_t wl = (size_t)wr * (DB * 16) * 64 + lane;
-      float* po = sp.o + (size_t)me * BM * D + wl;
+      float amax = 0.f;
 #pragma unroll
       for (int db = 0; db < DB; db++)
 #pragma unroll
-        for (int i = 0; i < 16; i++)
-          __hip_atomic_store(po + (db * 16 + i) * 64, o[db][i], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        for (int i = 0; i < 16; i++) amax = fmaxf(amax, fabsf(o[db][i]));
+      amax = half_swap_max(amax);
+      const float sinv = amax > 0.f ? 1.f / amax : 0.f;
+      typedef _Float16 h16x2 __attribute__((ext_vector_type(2)));
+      uint32_t yw[DB * 8];
+#pragma unroll
+      for (int db = 0; db < DB; db++)
+#pragma unroll
+        for (int i = 0; i < 16; i += 2)
+          yw[db * 8 + i / 2] =
+              __builtin_bit_cast(uint32_t, h16x2{(_Float16)(o[db][i] * sinv), (_Float16)(o[db][i + 1] * sinv)});
+      const size_t wl = (size_t)wr * (DB * 8) * 64 + lane;
+      uint32_t* po = sp.o + (size_t)me * (BM * D / 2) + wl;
+#pragma unroll
+      for (int j = 0; j < DB * 8; j++)
+        __hip_atomic_store(po + j * 64, yw[j], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       if (hf == 0) {
-        float* pm = sp.ml + ((size_t)me * BM + r) * 2;
+        float* pm = sp.ml + ((size_t)me * BM + r) * 4;
         __hip_atomic_store(pm, m_me, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
         __hip_atomic_store(pm + 1, l_tot, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+        __hip_atomic_store(pm + 2, amax, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       }
       __builtin_amdgcn_s_waitcnt(0x0F70);  // vmcnt(0) (expcnt, lgkmcnt not waited on): stores acknowledged
       __syncthreads();
@@ -624,11 +643,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         split_last = __hip_atomic_fetch_add(cnt, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM) == (int)(w1 - w0);
       __syncthreads();
       if (!split_last) return;
-      auto ld = [](const float* p) __attribute__((always_inline)) {
+      auto ldf = [](const float* p) __attribute__((always_inline)) {
         return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
       };
-      // merge in workgroup order (= key order), this piece from registers:
-      // the same arithmetic in the same order whichever workgroup merges
+      auto ldw = [](const uint32_t* p) __attribute__((always_inline)) {
+        return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_SYSTEM);
+      };
       // the tile starts inside workgroup w0's range (its last piece) or at its
       // first unit; for every later workgroup it is the first piece
       const long long s0 = 2LL * w0 + (seg_t0 > sp.wstart[w0] ? 1 : 0);
@@ -636,7 +656,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       float M = -1e30f;
       for (int ww = w0; ww <= w1; ww++) {
         const long long sl = slot_of(ww);
-        M = fmaxf(M, sl == me ? m_me : ld(sp.ml + ((size_t)sl * BM + r) * 2));
+        M = fmaxf(M, sl == me ? m_me : ldf(sp.ml + ((size_t)sl * BM + r) * 4));
       }
       f32x16 acc[DB];
 #pragma unroll
@@ -644,24 +664,31 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       float den = 0.f;
       for (int ww = w0; ww <= w1; ww++) {
         const long long sl = slot_of(ww);
+        float mc = m_me, lc = l_tot, sc = amax;
+        uint32_t xw[DB * 8];
         if (sl == me) {
-          const float e = m_me > -1e29f ? fast_exp2(m_me - M) : 0.f;
-          den = fmaf(e, l_tot, den);
 #pragma unroll
-          for (int db = 0; db < DB; db++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) acc[db][i] = fmaf(e, o[db][i], acc[db][i]);
+          for (int j = 0; j < DB * 8; j++) xw[j] = yw[j];
         } else {
-          const float* pm = sp.ml + ((size_t)sl * BM + r) * 2;
-          const float mc = ld(pm), lc = ld(pm + 1);
-          const float e = mc > -1e29f ? fast_exp2(mc - M) : 0.f;
-          den = fmaf(e, lc, den);
-          const float* pc = sp.o + (size_t)sl * BM * D + wl;
+          const float* pm = sp.ml + ((size_t)sl * BM + r) * 4;
+          mc = ldf(pm);
+          lc = ldf(pm + 1);
+          sc = ldf(pm + 2);
+          const uint32_t* pc = sp.o + (size_t)sl * (BM * D / 2) + wl;
 #pragma unroll
-          for (int db = 0; db < DB; db++)
-#pragma unroll
-            for (int i = 0; i < 16; i++) acc[db][i] = fmaf(e, ld(pc + (db * 16 + i) * 64), acc[db][i]);
+          for (int j = 0; j < DB * 8; j++) xw[j] = ldw(pc + j * 64);
         }
+        const float e = mc > -1e29f ? fast_exp2(mc - M) : 0.f;
+        den = fmaf(e, lc, den);
+        const float es = e * sc;
+#pragma unroll
+        for (int db = 0; db < DB; db++)
+#pragma unroll
+          for (int i = 0; i < 16; i += 2) {
+            const h16x2 y = __builtin_bit_cast(h16x2, xw[db * 8 + i / 2]);
+            acc[db][i] = fmaf(es, (float)y[0], acc[db][i]);
+            acc[db][i + 1] = fmaf(es, (float)y[1], acc[db][i + 1]);
+          }
       }
 #pragma unroll
       for (int db = 0; db < DB; db++) o[db] = acc[db];
@@ -781,7 +808,8 @@ size_t prefill_split_workspace_bytes(int B, int Sq, int Hq, int D, bool causal) 
   const KvSpec kv{};
   if (!split_applies(bh, Sq, causal, kv)) return 0;
   const grid::StreamPlan p = stream_plan_for(bh, Sq);
-  return kSplitCounterBytes + sizeof(float) * 2 * (size_t)p.G * kStreamBM * (size_t)(D + 2);
+  // per slot: BM x D fp16 values, then BM x 4 floats
+  return kSplitCounterBytes + 2 * (size_t)p.G * kStreamBM * (sizeof(uint16_t) * (size_t)D + 4 * sizeof(float));
 }
 
 hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
@@ -795,8 +823,8 @@ hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v
   const size_t nslots = 2 * (size_t)p.G;
   SplitArgs sa;
   sa.cnt = reinterpret_cast<int*>(ws);
-  sa.o = reinterpret_cast<float*>(static_cast<char*>(ws) + kSplitCounterBytes);
-  sa.ml = sa.o + nslots * kStreamBM * D;
+  sa.o = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kSplitCounterBytes);
+  sa.ml = reinterpret_cast<float*>(sa.o + nslots * kStreamBM * D / 2);
   sa.per = p.per;
   sa.cost = p.cost;
   sa.tile_cost = p.tile_cost;

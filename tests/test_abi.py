@@ -245,9 +245,9 @@ def test_binding_requires_device_tensors():
 def test_prefill_workspace_bytes():
     L = R.lib()
     # one GPU's 8-query-head share at 4096 tokens: stream-K over 256 workgroups,
-    # 4 KB of counters, then two partial states of 256 rows x (D + 2) floats per workgroup
+    # 4 KB of counters, then two partial states per workgroup: 256 rows x D fp16, 256 x 4 floats
     n = L.attn_prefill_workspace_bytes(1, 4096, 8, 128, 1)
-    assert n == 4096 + 256 * 2 * 256 * 130 * 4
+    assert n == 4096 + 256 * 2 * 256 * (2 * 128 + 16)
     assert L.attn_prefill_workspace_bytes(1, 4096, 8, 64, 1) < n
     assert L.attn_prefill_workspace_bytes(1, 4096, 8, 128, 0) == 0     # non-causal: no split
     assert L.attn_prefill_workspace_bytes(2, 4096, 64, 128, 1) == 0    # fills the GPU without one

@@ -658,26 +658,38 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
         const long long sl = slot_of(ww);
         M = fmaxf(M, sl == me ? m_me : ldf(sp.ml + ((size_t)sl * BM + r) * 4));
       }
+      // one piece's (m, l, scale, O words): this workgroup's from registers,
+      // the others' from memory; the next piece is fetched while the current
+      // one is added in
+      uint32_t xw[DB * 8];
+      float mc, lc, sc;
+      auto fetch = [&](int ww, uint32_t* w, float& m, float& l, float& sca) __attribute__((always_inline)) {
+        const long long sl = slot_of(ww);
+        if (sl == me) {
+          m = m_me;
+          l = l_tot;
+          sca = amax;
+#pragma unroll
+          for (int j = 0; j < DB * 8; j++) w[j] = yw[j];
+        } else {
+          const float* pm = sp.ml + ((size_t)sl * BM + r) * 4;
+          m = ldf(pm);
+          l = ldf(pm + 1);
+          sca = ldf(pm + 2);
+          const uint32_t* pc = sp.o + (size_t)sl * (BM * D / 2) + wl;
+#pragma unroll
+          for (int j = 0; j < DB * 8; j++) w[j] = ldw(pc + j * 64);
+        }
+      };
+      fetch(w0, xw, mc, lc, sc);
       f32x16 acc[DB];
 #pragma unroll
       for (int db = 0; db < DB; db++) acc[db] = f32x16{};
       float den = 0.f;
       for (int ww = w0; ww <= w1; ww++) {
-        const long long sl = slot_of(ww);
-        float mc = m_me, lc = l_tot, sc = amax;
-        uint32_t xw[DB * 8];
-        if (sl == me) {
-#pragma unroll
-          for (int j = 0; j < DB * 8; j++) xw[j] = yw[j];
-        } else {
-          const float* pm = sp.ml + ((size_t)sl * BM + r) * 4;
-          mc = ldf(pm);
-          lc = ldf(pm + 1);
-          sc = ldf(pm + 2);
-          const uint32_t* pc = sp.o + (size_t)sl * (BM * D / 2) + wl;
-#pragma unroll
-          for (int j = 0; j < DB * 8; j++) xw[j] = ldw(pc + j * 64);
-        }
+        uint32_t nw[DB * 8];
+        float mn = 0.f, ln = 0.f, sn = 0.f;
+        if (ww < w1) fetch(ww + 1, nw, mn, ln, sn);
         const float e = mc > -1e29f ? fast_exp2(mc - M) : 0.f;
         den = fmaf(e, lc, den);
         const float es = e * sc;
@@ -689,6 +701,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
             acc[db][i] = fmaf(es, (float)y[0], acc[db][i]);
             acc[db][i + 1] = fmaf(es, (float)y[1], acc[db][i + 1]);
           }
+        mc = mn;
+        lc = ln;
+        sc = sn;
+#pragma unroll
+        for (int j = 0; j < DB * 8; j++) xw[j] = nw[j];
       }
 #pragma unroll
       for (int db = 0; db < DB; db++) o[db] = acc[db];

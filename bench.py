@@ -424,7 +424,7 @@ def main():
         "roofline": {"bound": "mfma", "achieved": round(pre_tflops, 2), "peak": PEAK_BF16_TFLOPS,
                      "unit": "TFLOP/s", "frac": round(pre_tflops / PEAK_BF16_TFLOPS, 4),
                      "traffic": _traffic("prefill_c3", PREFILL_KERNEL_SRC),
-                     "kernel": "prefill_bf16_kernel<128, 8, false, 1, 64, false>", "launch_ms": round(float(pre_ms.mean()), 4)},
+                     "kernel": "prefill_bf16_kernel<128, 8, false, 1, 64, false, false>", "launch_ms": round(float(pre_ms.mean()), 4)},
         "decode": {"metric": "decode KV-cache GB/s", "value": round(dec_gbps, 1), "unit": "GB/s",
                    "launch_ms": round(float(dec_ms.mean()), 4),
                    "algorithmic_bytes": dec_bytes,

@@ -167,9 +167,9 @@ rcgqa_status attn_prefill(const void* q, const void* k, const void* v, void* out
 
 /*
  * attn_prefill_workspace_bytes -- bytes of scratch attn_prefill_ws needs for
- * these sizes.  Pure host function.  0 when the problem runs without one (it
- * is large enough for one workgroup per query tile, or not causal); returns 0
- * if an argument is not positive.
+ * these sizes.  Pure host function.  0 when the problem runs without one (see
+ * attn_prefill_ws: large, short or not causal); returns 0 if an argument is
+ * not positive.
  */
 size_t attn_prefill_workspace_bytes(int B, int S, int Hq, int head_dim, int causal);
 
@@ -180,15 +180,17 @@ size_t attn_prefill_workspace_bytes(int B, int S, int Hq, int head_dim, int caus
  *
  * Defines: as attn_prefill ([HF] section 1.2 steps 2-4 and section 2 steps
  * 4-5; repeat_kv head map).  For a causal bf16 problem too small to fill the
- * GPU with one workgroup per 256-row query tile (for example one GPU's
+ * GPU with pairs of heavy and light query tiles (for example one GPU's
  * 8-query-head / 1-KV-head share of a 64-head layer, the head split of [L2X]
- * section 3.1), the work is listed as (256-row query tile, 64-key tile)
- * steps and cut into 256 contiguous ranges of equal cost, one per
- * workgroup, which may cross query tiles (stream-K).  A query tile shared by
+ * section 3.1, or 16 query heads of 4096 tokens) but with at least 4096
+ * (256-row query tile, 64-key tile) steps, the steps are cut into 256
+ * contiguous ranges of equal cost, one per workgroup, which may cross query
+ * tiles (stream-K).  A query tile shared by
  * several workgroups is finished by the last of them to end: each writes its
  * softmax state (fp32 O, running max, row sum) to the workspace, and the
  * last merges the states in key order, so the result is repeatable bit for
- * bit.  Other problems (large, non-causal, fp32) run exactly as attn_prefill.
+ * bit.  Other problems (large, short, non-causal, longer than 32768 tokens,
+ * fp32) run exactly as attn_prefill.
  *
  * Arguments as attn_prefill, plus:
  * workspace  device buffer of at least attn_prefill_workspace_bytes(B, S, Hq,

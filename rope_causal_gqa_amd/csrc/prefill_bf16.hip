@@ -99,7 +99,7 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
 // per (batch, head), total cost and cost per tile start; the first unit of
 // every query tile of a (batch, head) block in list order (tstart[nqt] =
 // per) and of every workgroup (wstart[G] = all units), computed on the host.
-constexpr int kStreamMaxTiles = 64;   // query tiles per (batch, head)
+constexpr int kStreamMaxTiles = 128;  // query tiles per (batch, head): S up to 32768
 constexpr int kStreamMaxGroups = 256;
 struct SplitArgs {
   uint32_t* o;
@@ -791,17 +791,6 @@ static void launch_nw(const void* q, const void* k, const void* v, void* out, in
 }
 
 namespace {
-// Whether the launcher would take the key-group grids (one 8-wave workgroup
-// per CU) for this problem: the split-K path replaces them for causal
-// prefills without a cache or a mask.
-bool small_grid(long long bh, int Sq, bool causal, const KvSpec& kv) {
-  const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
-  const bool short_window = kv.window > 0 && kv.window < 2048;
-  const bool mask_ok = !kv.mask || (kv.msr % 8 == 0 && kv.msr >= 8);
-  if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512 && !short_window && mask_ok) return false;
-  const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;
-  return bh * (pair4 ? (nqt4 + 1) / 2 : nqt4) < 512;
-}
 // The split workspace starts with a fixed block of per-tile counters, so that
 // calls of any shape find theirs at the same place (zeroed by the last call);
 // the partial states follow it, two slots per workgroup.
@@ -810,10 +799,24 @@ constexpr size_t kSplitCounterBytes = kSplitCounters * sizeof(int);
 constexpr int kStreamBM = 256;     // 8-wave workgroups, one per CU
 constexpr int kStreamMinUnits = 4;  // units per workgroup at least
 constexpr int kStreamTileCost = 2;  // cost of a tile start, in units (its prologue; best of 0-6 measured)
+// Whether the launcher pairs heavy and light causal tiles (the 8-wave grid, or
+// the 4-wave grid when it has 512 pairs): those grids are as fast as stream-K.
+bool paired_grid(long long bh, int Sq) {
+  const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
+  return (nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512) || (nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512);
+}
+// Stream-K is used for causal prefills without a cache, window or mask that the
+// launcher would run on an unpaired grid, with at least kStreamMinShare units
+// per workgroup (below that the fixed cost of a piece outweighs the balance:
+// 8 heads of 2100 or 3000 tokens ran slower than the key-group grids, 8 heads
+// of 4096 and more faster).
+constexpr int kStreamMinShare = 16;
 bool split_applies(long long bh, int Sq, bool causal, const KvSpec& kv) {
-  return causal && !kv.lens && kv.window <= 0 && !kv.mask && small_grid(bh, Sq, causal, kv) &&
-         bh * ((Sq + kStreamBM - 1) / kStreamBM) <= kSplitCounters && (Sq + kStreamBM - 1) / kStreamBM <= kStreamMaxTiles &&
-         grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost).ok;
+  if (!causal || kv.lens || kv.window > 0 || kv.mask || paired_grid(bh, Sq)) return false;
+  const int nqt = (Sq + kStreamBM - 1) / kStreamBM;
+  if (nqt > kStreamMaxTiles || bh * nqt > kSplitCounters) return false;
+  const grid::StreamPlan p = grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost);
+  return p.ok && p.units >= (long long)kStreamMinShare * kStreamMaxGroups;
 }
 grid::StreamPlan stream_plan_for(long long bh, int Sq) {
   return grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost);

@@ -251,6 +251,10 @@ def test_prefill_workspace_bytes():
     assert L.attn_prefill_workspace_bytes(1, 4096, 8, 64, 1) < n
     assert L.attn_prefill_workspace_bytes(1, 4096, 8, 128, 0) == 0     # non-causal: no split
     assert L.attn_prefill_workspace_bytes(2, 4096, 64, 128, 1) == 0    # fills the GPU without one
+    assert L.attn_prefill_workspace_bytes(1, 4096, 32, 128, 1) == 0    # paired 4-wave grid
+    assert L.attn_prefill_workspace_bytes(1, 2100, 8, 128, 1) == 0     # too little work per workgroup
+    assert L.attn_prefill_workspace_bytes(1, 16384, 4, 128, 1) == n    # long: 256 workgroups too
+    assert L.attn_prefill_workspace_bytes(1, 32769, 2, 128, 1) == 0    # more than 128 query tiles
     assert L.attn_prefill_workspace_bytes(0, 4096, 8, 128, 1) == 0
     assert L.attn_prefill_workspace_bytes(1, 4096, 8, 96, 1) == 0
 

@@ -56,14 +56,14 @@ def test_full_size_all_heads():
 
 
 SPLIT = [
-    # B, S, Hq, Hkv, D: ragged tails, one query tile, D=64, several KV heads, B > 1
-    (1, 2100, 8, 1, 64),
-    (1, 2100, 8, 2, 128),
-    (1, 129, 16, 1, 128),
-    (1, 1, 1, 1, 128),
-    (2, 700, 4, 1, 128),
-    (1, 4096, 4, 4, 64),
-    (3, 1000, 2, 1, 128),
+    # B, S, Hq, Hkv, D (shapes the launcher would run on an unpaired grid, with at
+    # least 16 units of work per workgroup): ragged last tile with several KV
+    # heads, D=64, B > 1, Hkv = Hq, a ragged tail at B=3
+    (1, 2100, 32, 4, 128),
+    (1, 2048, 32, 4, 64),
+    (4, 2048, 8, 1, 128),
+    (2, 2048, 16, 16, 128),
+    (3, 1700, 16, 8, 128),
 ]
 
 
@@ -113,7 +113,7 @@ def test_repeatable_and_workspace_reuse_across_shapes():
         torch.cuda.synchronize()
         assert torch.equal(again, ref)
     _check_workspace(ws, need)
-    S2 = 1500
+    S2 = 4000
     q2, k2, v2 = (t[:, :S2].contiguous() for t in (q, k, v))
     small = R.attn_prefill_ws(q2, k2, v2, causal=True, scale=w.scale, workspace=ws)
     fresh = R.attn_prefill_ws(q2, k2, v2, causal=True, scale=w.scale)
@@ -128,6 +128,8 @@ def test_repeatable_and_workspace_reuse_across_shapes():
 @pytest.mark.parametrize("B,S,Hq,Hkv,D,causal,dtype", [
     (1, 2048, 8, 2, 128, False, "bf16"),   # not causal
     (2, 1000, 32, 8, 128, True, "bf16"),   # fills the GPU with one workgroup per tile
+    (1, 4096, 32, 8, 128, True, "bf16"),   # the paired 4-wave grid
+    (1, 2100, 8, 1, 128, True, "bf16"),    # too little work per workgroup
     (1, 300, 4, 1, 64, True, "fp32"),
 ])
 def test_runs_as_attn_prefill_otherwise(B, S, Hq, Hkv, D, causal, dtype):
@@ -143,3 +145,28 @@ def test_runs_as_attn_prefill_otherwise(B, S, Hq, Hkv, D, causal, dtype):
     b = R.attn_prefill_ws(qd, kd, vd, causal=causal, scale=D ** -0.5)
     torch.cuda.synchronize()
     assert torch.equal(a, b)
+
+
+@pytest.mark.parametrize("S,Hq", [(16384, 4), (32768, 2)])
+def test_long_sequence_sampled_rows(S, Hq):
+    """Long sequences (64 and 128 query tiles per head, the most the plan
+    takes): sampled rows against the oracle, each as a single query over its
+    visible keys (the single-query form of the same attention)."""
+    import torch
+    B, Hkv, D = 1, 1, 128
+    announce(f"split prefill long S={S} Hq={Hq}")
+    assert R.attn_prefill_workspace_bytes(B, S, Hq, D, True) > 0
+    seed = 700 + S
+    q = W.random_case(seed, (B, S, Hq, D), "bf16")
+    k = W.random_case(seed + 1, (B, S, Hkv, D), "bf16")
+    v = W.random_case(seed + 2, (B, S, Hkv, D), "bf16")
+    out = R.attn_prefill_ws(dev(q, "bf16"), dev(k, "bf16"), dev(v, "bf16"), causal=True, scale=D ** -0.5)
+    torch.cuda.synchronize()
+    got = host64(out)
+    assert np.all(np.isfinite(got))
+    k64 = np.transpose(W.to_f64(k, "bf16"), (0, 2, 1, 3))     # [B, Hkv, S, D] cache layout
+    v64 = np.transpose(W.to_f64(v, "bf16"), (0, 2, 1, 3))
+    q64 = W.to_f64(q, "bf16")
+    for i in [0, 255, 256, 4095, S // 2 + 13, S - 257, S - 1]:
+        ref = oracle.attention_cache(q64[:, i:i + 1], k64, v64, np.full(B, i + 1), True, D ** -0.5)
+        check(got[:, i:i + 1], ref, "bf16", f"split long S={S} row {i}")

@@ -18,7 +18,9 @@ peak; `decode.roofline` against HBM.  `chunked_prefill` and `sliding_window`
 time the two prefill extensions (attn_prefill_cache) separately, after the
 timed steps; `gqa_prefill` times attn_prefill on the LLaMA-70B-shaped GQA
 prefill (B=1 S=4096 Hq=64 Hkv=8 D=128) and, on its 8-query-head / 1-KV-head
-share, the stream-K entry point attn_prefill_ws (attn_prefill alongside); `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
+share, the stream-K entry point attn_prefill_ws (attn_prefill alongside);
+`stream_k_prefill` times attn_prefill_ws against attn_prefill on four more causal
+shapes that the launcher runs on unpaired grids; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
 entry points against the separate calls on the same workloads; `ntk_rope`
 times rope_apply at an NTK-aware scaled base; `masked_prefill` times
 attn_prefill_masked (causal plus a key-padding mask) on LLaMA-7B-shaped heads.  `cpu_baseline` times the float64 oracle on a bounded sample on
@@ -221,6 +223,27 @@ def _next_rows(R, dev, stream):
             gqa[name]["attn_prefill_tflops"] = round(w.flops() / (plain_ms * 1e-3) / 1e12, 2)
         del q, k, v, o
     out["gqa_prefill"] = [gqa["c4a"], gqa["c4b"]]
+    # attn_prefill_ws against attn_prefill on causal shapes the launcher runs on
+    # unpaired grids (one GPU's share of a head split, long single sequences)
+    rows = []
+    for B, S, Hq, Hkv in ((1, 4096, 16, 2), (1, 8192, 8, 1), (1, 16384, 4, 1), (4, 2048, 8, 1)):
+        D = 128
+        q = torch.randn((B, S, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+        k = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        v = torch.randn((B, S, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+        o = torch.empty_like(q)
+        wsp = torch.zeros(max(R.attn_prefill_workspace_bytes(B, S, Hq, D, True), 1), dtype=torch.uint8, device=dev)
+        ws_ms = _time_launches(lambda: R.attn_prefill_ws(q, k, v, o, causal=True, scale=D ** -0.5, workspace=wsp),
+                               stream)
+        ms = _time_launches(lambda: R.attn_prefill(q, k, v, o, causal=True, scale=D ** -0.5), stream)
+        flops = 4.0 * D * Hq * B * (S * (S + 1) / 2)
+        rows.append({"workload": f"B={B} S={S} Hq={Hq} Hkv={Hkv} D={D} bf16 causal",
+                     "attn_prefill_ws_ms": round(ws_ms, 4), "attn_prefill_ms": round(ms, 4),
+                     "attn_prefill_ws_tflops": round(flops / (ws_ms * 1e-3) / 1e12, 2),
+                     "attn_prefill_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "speedup": round(ms / ws_ms, 3)})
+        del q, k, v, o, wsp
+    out["stream_k_prefill"] = rows
     return out
 
 
@@ -437,6 +460,7 @@ def main():
         "chunked_prefill": extras.get("chunked_prefill"),
         "sliding_window": extras.get("sliding_window"),
         "gqa_prefill": extras.get("gqa_prefill"),
+        "stream_k_prefill": extras.get("stream_k_prefill"),
         "masked_prefill": extras.get("masked_prefill"),
         "fused_rope_prefill": fused.get("fused_rope_prefill"),
         "fused_rope_decode": fused.get("fused_rope_decode"),

@@ -370,26 +370,46 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       const bf16* sk = ldsg + buf * 2 * TILE;
       const bf16* sv = sk + TILE;
 
-      // S^T = K Q^T - m_ref: NKB 32-key blocks, chains interleaved
+      // S^T = K Q^T - m_ref: NKB 32-key blocks, chains interleaved, the K
+      // operand reads kept PREF products ahead of the MFMAs.
       f32x16 s[NKB];
+      constexpr int NP = NKB * KS;  // products of the step, kb2 fastest
+      auto kread = [&](int i) __attribute__((always_inline)) {
+        return *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(sk) + koff[i / NKB] +
+                                                (i % NKB) * 32 * D * (int)sizeof(bf16));
+      };
+      if constexpr (SPL) {
+        // Through an explicit ring of PREF registers with a scheduling barrier
+        // after each product: in this instantiation the scheduler otherwise
+        // moves every read down to its product and waits for each one.
+        bf16x8 kring[PREF];
 #pragma unroll
-      for (int ks = 0; ks < KS; ks++) {
+        for (int i = 0; i < PREF; i++) kring[i] = kread(i);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int kb2 = 0; kb2 < NKB; kb2++) {
-          const bf16x8 a = *reinterpret_cast<const bf16x8*>(reinterpret_cast<const char*>(sk) + koff[ks] +
-                                                            kb2 * 32 * D * (int)sizeof(bf16));
-          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, qf[ks], ks > 0 ? s[kb2] : NEGM ? negm : f32x16{}, 0,
-                                                           0, 0);
+        for (int i = 0; i < NP; i++) {
+          const int ks = i / NKB, kb2 = i % NKB;
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kring[i % PREF], qf[ks],
+                                                           ks > 0 ? s[kb2] : NEGM ? negm : f32x16{}, 0, 0, 0);
+          if (i + PREF < NP) kring[i % PREF] = kread(i + PREF);
+          __builtin_amdgcn_sched_barrier(0);
         }
-      }
-      if (PREF > 0) {
-        __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PREF, 0);
+      } else {
 #pragma unroll
-        for (int i = 0; i < NKB * KS - PREF; i++) {
-          __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
-          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+        for (int i = 0; i < NP; i++) {
+          const int ks = i / NKB, kb2 = i % NKB;
+          s[kb2] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(kread(i), qf[ks], ks > 0 ? s[kb2] : NEGM ? negm : f32x16{},
+                                                           0, 0, 0);
         }
-        __builtin_amdgcn_sched_group_barrier(kSchedMfma, PREF, 0);
+        if (PREF > 0) {
+          __builtin_amdgcn_sched_group_barrier(kSchedDsRead, PREF, 0);
+#pragma unroll
+          for (int i = 0; i < NP - PREF; i++) {
+            __builtin_amdgcn_sched_group_barrier(kSchedMfma, 1, 0);
+            __builtin_amdgcn_sched_group_barrier(kSchedDsRead, 1, 0);
+          }
+          __builtin_amdgcn_sched_group_barrier(kSchedMfma, PREF, 0);
+        }
       }
 
       // the first 16-key chunk of P.V operands is read now, so its latency

@@ -20,13 +20,18 @@ def _i32(a):
 
 def test_graph_prefill_paths():
     """rope_apply + attn_prefill (8-wave grid), attn_prefill on a four-key-group
-    grid and rope_attn_prefill, captured together."""
+    grid, attn_prefill_ws (stream-K: per-tile counters that every call leaves
+    at zero, so replays find them ready) and rope_attn_prefill, captured
+    together."""
     import torch
     announce("graph: prefill paths")
     B, S, Hq, Hkv, D = 2, 2048, 32, 32, 128      # paired 8-wave grid
     q, k, v = (dev(W.random_case(s, (B, S, h, D), "bf16"), "bf16") for s, h in ((1, Hq), (2, Hkv), (3, Hkv)))
     q2, k2, v2 = (dev(W.random_case(s, (1, 2100, h, D), "bf16"), "bf16") for s, h in ((4, 8), (5, 1), (6, 1)))
-    out, out2 = torch.empty_like(q), torch.empty_like(q2)
+    q3, k3, v3 = (dev(W.random_case(s, (1, 4096, h, D), "bf16"), "bf16") for s, h in ((8, 8), (9, 1), (10, 1)))
+    out, out2, out3 = torch.empty_like(q), torch.empty_like(q2), torch.empty_like(q3)
+    wsk = torch.zeros(R.attn_prefill_workspace_bytes(1, 4096, 8, D, True), dtype=torch.uint8, device="cuda")
+    assert wsk.numel() > 0
     qf, kf = q.clone(), k.clone()
     outf = torch.empty_like(q)
     ws = torch.empty(R.rope_attn_prefill_workspace_bytes(B, S, D), dtype=torch.uint8, device="cuda")
@@ -35,13 +40,14 @@ def test_graph_prefill_paths():
         R.rope_apply(q, k, None, 1e4, 1.0)
         R.attn_prefill(q, k, v, out, causal=True, scale=D ** -0.5)
         R.attn_prefill(q2, k2, v2, out2, causal=True, scale=D ** -0.5)
+        R.attn_prefill_ws(q3, k3, v3, out3, causal=True, scale=D ** -0.5, workspace=wsk)
         R.rope_attn_prefill(qf, kf, v, None, outf, causal=True, scale=D ** -0.5, theta=1e4, workspace=ws)
 
-    srcs = [tuple(dev(W.random_case(100 * r + s, t.shape, "bf16"), "bf16") for s, t in enumerate((q, k, v, q2, k2, v2)))
-            for r in range(3)]
+    srcs = [tuple(dev(W.random_case(100 * r + s, t.shape, "bf16"), "bf16")
+                  for s, t in enumerate((q, k, v, q2, k2, v2, q3, k3, v3))) for r in range(3)]
 
     def load(r):
-        for dst, src in zip((q, k, v, q2, k2, v2), srcs[r]):
+        for dst, src in zip((q, k, v, q2, k2, v2, q3, k3, v3), srcs[r]):
             dst.copy_(src)
         qf.copy_(srcs[r][0])
         kf.copy_(srcs[r][1])
@@ -52,7 +58,7 @@ def test_graph_prefill_paths():
         load(r)
         calls()
         torch.cuda.synchronize()
-        refs.append([t.clone() for t in (q, k, out, out2, kf, outf)])
+        refs.append([t.clone() for t in (q, k, out, out2, out3, kf, outf)])
     # capture (after a warm-up on the side stream, as torch requires)
     load(0)
     s = torch.cuda.Stream()
@@ -71,7 +77,7 @@ def test_graph_prefill_paths():
             torch.cuda.synchronize()
             g.replay()
             torch.cuda.synchronize()
-            for got, ref in zip((q, k, out, out2, kf, outf), refs[r]):
+            for got, ref in zip((q, k, out, out2, out3, kf, outf), refs[r]):
                 assert torch.equal(got, ref), f"replay {rep}/{r} differs from the eager calls"
 
 

@@ -274,6 +274,44 @@ rcgqa_status attn_prefill_cache(const void* q, const void* k_cache, const void* 
                                 rcgqa_dtype dt, rcgqa_stream stream);
 
 /*
+ * attn_prefill_cache_workspace_bytes -- bytes of scratch attn_prefill_cache_ws
+ * needs for these sizes.  Pure host function.  0 when the problem runs
+ * without one (see attn_prefill_cache_ws); 0 if an argument is not positive.
+ */
+size_t attn_prefill_cache_workspace_bytes(int B, int Sq, int Hq, int head_dim, int max_kv, int causal,
+                                          int window);
+
+/*
+ * attn_prefill_cache_ws -- attn_prefill_cache with a caller-owned workspace,
+ * which lets causal chunks without a window spread their work over all
+ * workgroups.
+ *
+ * Defines: as attn_prefill_cache ([HF] section 1.2 steps 2-4 and section 2
+ * steps 4-5 over the cached keys; [L2] "KV cache").  For a causal bf16 block
+ * with no window, max_kv >= Sq, and too few query tiles to fill the GPU with
+ * pairs of them (for example a chunk of 512 new tokens after 4096 cached
+ * ones), the work is listed as (256-row query tile, 64-key tile) steps,
+ * counted as if every sequence held max_kv rows, and cut into 256 contiguous
+ * ranges of equal cost, one per workgroup (stream-K, as attn_prefill_ws).
+ * Shorter sequences are still exact: the steps past their keys are skipped.
+ * A query tile shared by several workgroups is merged by the last of them in
+ * key order, so the result repeats bit for bit.  Other problems run exactly
+ * as attn_prefill_cache.
+ *
+ * Arguments as attn_prefill_cache, plus workspace / workspace_bytes with the
+ * contract of attn_prefill_ws (at least attn_prefill_cache_workspace_bytes
+ * bytes, 256-byte aligned, its first 4096 bytes zero before the first use
+ * and left zero by every call; not shared by concurrent calls).  Errors as
+ * attn_prefill_cache; a workspace that is too small, misaligned, null when
+ * needed or equal to another argument is RCGQA_EINVAL (nothing launched).
+ */
+rcgqa_status attn_prefill_cache_ws(const void* q, const void* k_cache, const void* v_cache,
+                                   const int32_t* kv_lens, void* out,
+                                   int B, int Sq, int Hq, int Hkv, int head_dim, int max_kv,
+                                   int causal, int window, float scale, rcgqa_dtype dt,
+                                   void* workspace, size_t workspace_bytes, rcgqa_stream stream);
+
+/*
  * attn_decode_workspace_bytes -- bytes of scratch attn_decode needs for these
  * sizes (partial softmax states of the split-K pass).  Pure host function.
  * Returns 0 if an argument is not positive.

@@ -7,11 +7,13 @@ it never computes any step itself.  The library is loaded on first use and a
 missing or unloadable library raises immediately.
 """
 from ._binding import (RcgqaError, attn_decode, attn_decode_noalloc, attn_decode_workspace_bytes, attn_prefill,
-                       attn_prefill_cache, attn_prefill_masked, attn_prefill_workspace_bytes, attn_prefill_ws, kv_append, lib, lib_path, rope_apply, rope_apply_interleaved,
+                       attn_prefill_cache, attn_prefill_cache_workspace_bytes, attn_prefill_cache_ws,
+                       attn_prefill_masked, attn_prefill_workspace_bytes, attn_prefill_ws, kv_append, lib, lib_path, rope_apply, rope_apply_interleaved,
                        rope_attn_decode, rope_attn_decode_workspace_bytes, rope_attn_prefill,
                        rope_attn_prefill_workspace_bytes, rope_dynamic_ntk_theta, rope_ntk_theta)
 
 __all__ = ["RcgqaError", "attn_decode", "attn_decode_noalloc", "attn_decode_workspace_bytes", "attn_prefill",
-           "attn_prefill_cache", "attn_prefill_masked", "attn_prefill_workspace_bytes", "attn_prefill_ws", "kv_append", "lib", "lib_path", "rope_apply", "rope_apply_interleaved",
+           "attn_prefill_cache", "attn_prefill_cache_workspace_bytes", "attn_prefill_cache_ws",
+           "attn_prefill_masked", "attn_prefill_workspace_bytes", "attn_prefill_ws", "kv_append", "lib", "lib_path", "rope_apply", "rope_apply_interleaved",
            "rope_attn_decode", "rope_attn_decode_workspace_bytes", "rope_attn_prefill",
            "rope_attn_prefill_workspace_bytes", "rope_dynamic_ntk_theta", "rope_ntk_theta"]

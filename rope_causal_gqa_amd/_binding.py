@@ -51,6 +51,11 @@ def lib():
     L.attn_prefill_masked.restype = i32
     L.attn_prefill_cache.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp]
     L.attn_prefill_cache.restype = i32
+    L.attn_prefill_cache_workspace_bytes.argtypes = [i32, i32, i32, i32, i32, i32, i32]
+    L.attn_prefill_cache_workspace_bytes.restype = sz
+    L.attn_prefill_cache_ws.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, i32, i32, i32, f32, i32, vp, sz,
+                                        vp]
+    L.attn_prefill_cache_ws.restype = i32
     L.attn_decode_workspace_bytes.argtypes = [i32, i32, i32, i32]
     L.attn_decode_workspace_bytes.restype = sz
     L.attn_decode.argtypes = [vp, vp, vp, vp, vp, i32, i32, i32, i32, i32, f32, i32, vp, sz, vp]
@@ -253,6 +258,38 @@ def attn_prefill_cache(q, k_cache, v_cache, kv_lens, out=None, causal=True, *, s
                                   _dev(out, "out", dt, 4), B, Sq, Hq, Hkv, D, max_kv, int(bool(causal)),
                                   int(window), float(scale), dt, _stream(q))
     _check(st, "attn_prefill_cache")
+    return out
+
+
+def attn_prefill_cache_workspace_bytes(B, Sq, Hq, head_dim, max_kv, causal=True, window=0):
+    return int(lib().attn_prefill_cache_workspace_bytes(B, Sq, Hq, head_dim, max_kv, int(bool(causal)), int(window)))
+
+
+def attn_prefill_cache_ws(q, k_cache, v_cache, kv_lens, out=None, causal=True, *, scale, window=0, workspace=None):
+    """attn_prefill_cache with a caller-owned workspace (stream-K for causal
+    chunks without a window; see rcgqa.h).  ``workspace`` (uint8, at least
+    attn_prefill_cache_workspace_bytes) must be zeroed before its first use;
+    every call leaves it ready for the next.  Without one a zeroed buffer is
+    allocated for this call."""
+    import torch
+    dt = _dtype_code(q)
+    B, Sq, Hq, D = q.shape
+    _, Hkv, max_kv, _ = k_cache.shape
+    if tuple(k_cache.shape) != (B, Hkv, max_kv, D) or tuple(v_cache.shape) != (B, Hkv, max_kv, D):
+        raise ValueError("caches must be [B, Hkv, max_kv, D] matching q")
+    if out is None:
+        out = torch.empty_like(q)
+    if tuple(out.shape) != (B, Sq, Hq, D):
+        raise ValueError("out must be [B, Sq, Hq, D]")
+    if workspace is None:
+        need = attn_prefill_cache_workspace_bytes(B, Sq, Hq, D, max_kv, causal, window) if dt == BF16 else 0
+        workspace = torch.zeros(max(need, 1), dtype=torch.uint8, device=q.device)
+    wbytes = workspace.numel() * workspace.element_size()
+    st = lib().attn_prefill_cache_ws(_dev(q, "q", dt, 4), _dev(k_cache, "k_cache", dt, 4),
+                                     _dev(v_cache, "v_cache", dt, 4), _i32(kv_lens, "kv_lens", B),
+                                     _dev(out, "out", dt, 4), B, Sq, Hq, Hkv, D, max_kv, int(bool(causal)),
+                                     int(window), float(scale), dt, _dev(workspace, "workspace"), wbytes, _stream(q))
+    _check(st, "attn_prefill_cache_ws")
     return out
 
 

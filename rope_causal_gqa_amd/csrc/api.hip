@@ -170,6 +170,47 @@ rcgqa_status attn_prefill_ws(const void* q, const void* k, const void* v, void* 
                                               Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr, st));
 }
 
+size_t attn_prefill_cache_workspace_bytes(int B, int Sq, int Hq, int head_dim, int max_kv, int causal, int window) {
+  if (!pos_int(B) || !pos_int(Sq) || !pos_int(Hq) || !pos_int(head_dim) || !pos_int(max_kv) || window < 0) return 0;
+  if (mul({B, Hq}) > kI32Max || !attn_head_dim(head_dim)) return 0;
+  if (window >= max_kv) window = 0;
+  return rcgqa::prefill_cache_split_workspace_bytes(B, Sq, Hq, head_dim, max_kv, causal != 0, window);
+}
+
+rcgqa_status attn_prefill_cache_ws(const void* q, const void* k_cache, const void* v_cache, const int32_t* kv_lens,
+                                   void* out, int B, int Sq, int Hq, int Hkv, int head_dim, int max_kv, int causal,
+                                   int window, float scale, rcgqa_dtype dt, void* workspace, size_t workspace_bytes,
+                                   rcgqa_stream stream) {
+  if (!q || !k_cache || !v_cache || !kv_lens || !out || !good_dtype(dt)) return RCGQA_EINVAL;
+  if (!al16({q, k_cache, v_cache, out}) || !al4(kv_lens)) return RCGQA_EINVAL;
+  if (out == q || out == k_cache || out == v_cache) return RCGQA_EINVAL;
+  if (!pos_int(B) || !pos_int(Sq) || !pos_int(Hq) || !pos_int(Hkv) || Hq % Hkv || !pos_int(max_kv))
+    return RCGQA_EINVAL;
+  if (head_dim < 2 || head_dim % 2 || (causal != 0 && causal != 1) || !finite_pos(scale)) return RCGQA_EINVAL;
+  if (window < 0 || (window > 0 && causal == 0)) return RCGQA_EINVAL;
+  if (mul({B, Hq}) > kI32Max || mul({B, Sq, Hq, head_dim}) < 0 || mul({B, Hkv, max_kv, head_dim}) < 0)
+    return RCGQA_EINVAL;
+  if (!attn_head_dim(head_dim) || !prefill_grid_ok(B, Hq, Sq)) return RCGQA_EUNSUPPORTED;
+  if (window >= max_kv) window = 0;  // as attn_prefill_cache: no key is excluded
+  const size_t need =
+      dt == RCGQA_BF16 ? rcgqa::prefill_cache_split_workspace_bytes(B, Sq, Hq, head_dim, max_kv, causal != 0, window)
+                       : 0;
+  if (need && (!workspace || workspace_bytes < need || reinterpret_cast<uintptr_t>(workspace) % 256))
+    return RCGQA_EINVAL;
+  if (workspace && (workspace == q || workspace == k_cache || workspace == v_cache || workspace == out ||
+                    workspace == kv_lens))
+    return RCGQA_EINVAL;
+  const hipStream_t st = (hipStream_t)stream;
+  const rcgqa::KvSpec kv{(long long)Hkv * max_kv * head_dim, (long long)max_kv * head_dim, head_dim, kv_lens,
+                         max_kv, window};
+  if (dt == RCGQA_BF16)
+    return hip_status(rcgqa::launch_prefill_bf16_split(q, k_cache, v_cache, out, B, Sq, Hq, Hkv, head_dim,
+                                                       causal != 0, scale, kv, need ? workspace : nullptr, st));
+  return hip_status(rcgqa::launch_prefill_f32((const float*)q, (const float*)k_cache, (const float*)v_cache,
+                                              (float*)out, B, Sq, Hq, Hkv, head_dim, causal != 0, scale, kv, nullptr,
+                                              st));
+}
+
 rcgqa_status attn_prefill_masked(const void* q, const void* k, const void* v, const void* mask, void* out, int B,
                                  int S, int Hq, int Hkv, int head_dim, int mask_heads, int mask_ld, int causal,
                                  float scale, rcgqa_dtype dt, rcgqa_stream stream) {

@@ -101,8 +101,11 @@ inline KeyGroupGrid key_group_grid(long long bh, int Sq, bool causal, long long 
 // is used only where C(units) G fits), constexpr so that the kernel runs
 // this code: every (batch, head) block has the same layout, so each step is
 // one division and a walk over one block's tiles.
-constexpr int stream_ntiles(int Sq, int qt, int BM) {
-  return ((Sq < BM * (qt + 1) ? Sq : BM * (qt + 1)) + 63) / 64;
+// Key tiles that query tile qt sees when query row i sits at key position
+// i + off (off = keys before the first query row: 0 for a plain prefill, the
+// cached tokens before the chunk for a prefill against a cache).
+constexpr int stream_ntiles(int Sq, int qt, int BM, int off = 0) {
+  return ((Sq < BM * (qt + 1) ? Sq : BM * (qt + 1)) + off + 63) / 64;
 }
 // query tile of list position j within a (batch, head) block
 constexpr int stream_pair_qt(int j, int nqt) { return (j & 1) ? (j >> 1) : nqt - 1 - (j >> 1); }
@@ -117,10 +120,10 @@ struct StreamPlan {
   bool ok;        // the sizes fit the 32-bit arithmetic
 };
 
-inline StreamPlan stream_plan(long long bh, int Sq, int BM, int slots, int min_units, int tile_cost) {
+inline StreamPlan stream_plan(long long bh, int Sq, int BM, int slots, int min_units, int tile_cost, int off = 0) {
   const int nqt = (Sq + BM - 1) / BM;
   long long per = 0;
-  for (int qt = 0; qt < nqt; qt++) per += stream_ntiles(Sq, qt, BM);
+  for (int qt = 0; qt < nqt; qt++) per += stream_ntiles(Sq, qt, BM, off);
   const long long units = bh * per, cost = units + (long long)tile_cost * bh * nqt;
   // at least min_units units and more than tile_cost + 1 of cost per workgroup, so that no range is empty
   const long long G =
@@ -135,29 +138,30 @@ inline StreamPlan stream_plan(long long bh, int Sq, int BM, int slots, int min_u
 struct StreamTile {
   int bh, qt, k, n, t0, tile, before;
 };
-constexpr StreamTile stream_tile(int u, int nqt, int per, int Sq, int BM) {
+constexpr StreamTile stream_tile(int u, int nqt, int per, int Sq, int BM, int off = 0) {
   const int b = u / per, r = u - b * per;
   int s = 0, j = 0;
   for (; j < nqt - 1; j++) {
-    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM);
+    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM, off);
     if (r < s + n) break;
     s += n;
   }
   const int qt = stream_pair_qt(j, nqt);
-  return {b, qt, r - s, stream_ntiles(Sq, qt, BM), b * per + s, b * nqt + qt, b * nqt + j};
+  return {b, qt, r - s, stream_ntiles(Sq, qt, BM, off), b * per + s, b * nqt + qt, b * nqt + j};
 }
 
 // C(u) for 0 <= u <= units
-constexpr int stream_cost(int u, int units, int nqt, int per, int Sq, int BM, int tile_cost) {
+constexpr int stream_cost(int u, int units, int nqt, int per, int Sq, int BM, int tile_cost, int off = 0) {
   if (u >= units) return units + tile_cost * (units / per) * nqt;
-  const StreamTile t = stream_tile(u, nqt, per, Sq, BM);
+  const StreamTile t = stream_tile(u, nqt, per, Sq, BM, off);
   return u + tile_cost * (t.before + (u > t.t0 ? 1 : 0));
 }
 
 // First unit of workgroup w (w = G gives `units`): the first u with
 // C(u) >= c = ceil(w cost / G), found in the (batch, head) block that c
 // falls in (each block adds per + tile_cost nqt to C)
-constexpr int stream_start(int w, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost) {
+constexpr int stream_start(int w, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost,
+                           int off = 0) {
   const int c = (w * cost + G - 1) / G;
   const int cb = per + tile_cost * nqt;
   const int b = c / cb, rem = c - b * cb;
@@ -165,7 +169,7 @@ constexpr int stream_start(int w, int G, int units, int cost, int nqt, int per, 
   int s = 0;
   for (int j = 0; j < nqt; j++) {
     if (rem <= s + tile_cost * j) return b * per + s;  // at tile j's first unit
-    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM);
+    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM, off);
     if (rem <= s + n + tile_cost * (j + 1)) {           // inside tile j: C = u + tile_cost (j + 1)
       const int r = rem - tile_cost * (j + 1);
       return b * per + (r > s + 1 ? r : s + 1);
@@ -176,8 +180,9 @@ constexpr int stream_start(int w, int G, int units, int cost, int nqt, int per, 
 }
 
 // Workgroup that runs unit u (u < units)
-constexpr int stream_owner(int u, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost) {
-  return stream_cost(u, units, nqt, per, Sq, BM, tile_cost) * G / cost;
+constexpr int stream_owner(int u, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost,
+                           int off = 0) {
+  return stream_cost(u, units, nqt, per, Sq, BM, tile_cost, off) * G / cost;
 }
 
 }  // namespace grid

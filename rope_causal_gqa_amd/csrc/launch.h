@@ -61,6 +61,9 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
 // call, and every call leaves them zero.  Falls back to launch_prefill_bf16
 // when the split is not used.
 size_t prefill_split_workspace_bytes(int B, int Sq, int Hq, int D, bool causal);
+// The same for a prefill of Sq query rows against a cache of max_kv rows
+// (launch_prefill_bf16_split with kv.lens set).
+size_t prefill_cache_split_workspace_bytes(int B, int Sq, int Hq, int D, int max_kv, bool causal, int window);
 hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
                                      int Hkv, int D, bool causal, float scale, const KvSpec& kv, void* ws,
                                      hipStream_t st);

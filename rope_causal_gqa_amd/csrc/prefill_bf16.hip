@@ -172,10 +172,12 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int item = (total & 7) == 0 ? (wid & 7) * (total >> 3) + (wid >> 3) : wid;
   const size_t qrs = (size_t)Hq * D, kvrs = (size_t)kv.sr;
   // One query tile of (batch, head) bh at rows [q0, q0 + BM).  SPL: key tiles
-  // [seg_lo, seg_hi) of the tile, which starts at unit seg_t0, has counter
-  // seg_tile and seg_before tiles before it in the list; this workgroup's
-  // range starts at unit seg_a.
-  auto run_qtile = [&](const int q0, const int bh, const int seg_lo, const int seg_hi, const int seg_t0,
+  // [seg_lo, seg_hi) of the tile, which the plan gives seg_n key tiles (a
+  // sequence shorter than the plan assumes has fewer visible ones; the rest
+  // are skipped) and which starts at unit seg_t0, has counter seg_tile and
+  // seg_before tiles before it in the list; this workgroup's range starts at
+  // unit seg_a.
+  auto run_qtile = [&](const int q0, const int bh, const int seg_lo, const int seg_hi, const int seg_n, const int seg_t0,
                        const int seg_tile, const int seg_before, const int seg_a) __attribute__((always_inline)) {
   const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / (Hq / Hkv);
@@ -325,11 +327,13 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   const int key_lo = (causal && W > 0) ? max(0, q0 + off - W + 1) : 0;
   const int t_lo = key_lo / BN, t_hi = key_hi > 0 ? (key_hi + BN - 1) / BN : 0;
   // this group's tiles [tg_lo, tg_hi) (possibly empty); all groups run `steps` barrier steps.
-  // A stream-K piece takes the tiles [seg_lo, seg_hi) of its range (t_lo = 0 there).
+  // A stream-K piece takes the tiles [seg_lo, seg_hi) of its range (t_lo = 0
+  // there), cut at t_hi: against a cache, a sequence shorter than the plan
+  // assumes has fewer key tiles, and none past them is ever loaded.
   const int ntl = max(t_hi - t_lo, 0);
-  const int steps = SPL ? seg_hi - seg_lo : (ntl + KSPLIT - 1) / KSPLIT;
-  const int tg_lo = SPL ? seg_lo : t_lo + grp * steps;
-  const int tg_hi = SPL ? seg_hi : min(tg_lo + steps, t_lo + ntl);
+  const int tg_lo = SPL ? min(seg_lo, t_hi) : t_lo + grp * ((ntl + KSPLIT - 1) / KSPLIT);
+  const int tg_hi = SPL ? min(seg_hi, t_hi) : min(tg_lo + (ntl + KSPLIT - 1) / KSPLIT, t_lo + ntl);
+  const int steps = SPL ? tg_hi - tg_lo : (ntl + KSPLIT - 1) / KSPLIT;
   const int wrow_lo = q0 + wr * 32, wrow_hi = wrow_lo + 31;
 
   // transpose-read addressing of V (fixed per lane)
@@ -608,7 +612,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     // owner of unit u: C(u) G / cost, with C(u) = u + tile_cost (tiles started before u)
     const int G = total;
     const int w0 = (seg_t0 + sp.tile_cost * seg_before) * G / sp.cost;
-    const int w1 = (seg_t0 + ntl - 1 + sp.tile_cost * (seg_before + (ntl > 1 ? 1 : 0))) * G / sp.cost;
+    const int w1 = (seg_t0 + seg_n - 1 + sp.tile_cost * (seg_before + (seg_n > 1 ? 1 : 0))) * G / sp.cost;
     if (w1 > w0) {
       // The pieces run on any XCD, and each XCD has its own L2, so the
       // hand-over goes through memory without whole-cache maintenance (an L2
@@ -764,7 +768,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
       const int qt = grid::stream_pair_qt(lo, nqt);
       const int t0 = b_ * sp.per + sp.tstart[lo], n = sp.tstart[lo + 1] - sp.tstart[lo], k0 = r - sp.tstart[lo];
       const int k_hi = min(n, k0 + (u_end - u));
-      run_qtile(qt * BM, b_, k0, k_hi, t0, b_ * nqt + qt, b_ * nqt + lo, u_a);
+      run_qtile(qt * BM, b_, k0, k_hi, n, t0, b_ * nqt + qt, b_ * nqt + lo, u_a);
       u += k_hi - k0;
     }
   } else {
@@ -772,8 +776,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     // heavy (late) causal query tiles first: with more workgroups than fit at
     // once, the light ones then fill in behind them
     const int qt_first = (npairs < nqt || causal) ? nqt - 1 - slot : slot;
-    run_qtile(qt_first * BM, bh, 0, 0, 0, 0, 0, 0);
-    if (npairs < nqt && slot != nqt - 1 - slot) run_qtile(slot * BM, bh, 0, 0, 0, 0, 0, 0);
+    run_qtile(qt_first * BM, bh, 0, 0, 0, 0, 0, 0, 0);
+    if (npairs < nqt && slot != nqt - 1 - slot) run_qtile(slot * BM, bh, 0, 0, 0, 0, 0, 0, 0);
   }
 }
 
@@ -825,31 +829,52 @@ bool paired_grid(long long bh, int Sq) {
   const int nqt8 = (Sq + 255) / 256, nqt4 = (Sq + 127) / 128;
   return (nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512) || (nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512);
 }
-// Stream-K is used for causal prefills without a cache, window or mask that the
-// launcher would run on an unpaired grid, with at least kStreamMinShare units
-// per workgroup (below that the fixed cost of a piece outweighs the balance:
-// 8 heads of 2100 or 3000 tokens ran slower than the key-group grids, 8 heads
-// of 4096 and more faster).
+// Stream-K is used for causal prefills without a window or mask (plain, or
+// against a cache of max_kv >= Sq rows, see below) that the launcher would
+// run on an unpaired grid, with at least kStreamMinShare units per workgroup (below
+// that the fixed cost of a piece outweighs the balance: 8 heads of 2100 or
+// 3000 tokens ran slower than the key-group grids, 8 heads of 4096 and more
+// faster).  Against a cache the plan assumes every sequence holds max_kv
+// rows (query row i at key position max_kv - Sq + i): shorter sequences
+// stay correct and only leave part of their pieces idle.
 constexpr int kStreamMinShare = 16;
+int stream_off(int Sq, const KvSpec& kv) { return kv.lens ? kv.max_kv - Sq : 0; }
+grid::StreamPlan stream_plan_for(long long bh, int Sq, int off) {
+  return grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost, off);
+}
 bool split_applies(long long bh, int Sq, bool causal, const KvSpec& kv) {
-  if (!causal || kv.lens || kv.window > 0 || kv.mask || paired_grid(bh, Sq)) return false;
+  if (!causal || kv.window > 0 || kv.mask || paired_grid(bh, Sq)) return false;
+  // Against a long cache every query tile does about the same work, so the
+  // key-group grid is balanced once it has a workgroup per CU (a chunk of 512
+  // after 4096 cached tokens, 64 heads: 80 us there against 83 us stream-K);
+  // below that stream-K wins (8 heads, 2048 after 6144 cached: 1.21x).
+  if (kv.lens && (kv.max_kv < Sq || bh * ((Sq + 127) / 128) >= grid::kCUs)) return false;
   const int nqt = (Sq + kStreamBM - 1) / kStreamBM;
   if (nqt > kStreamMaxTiles || bh * nqt > kSplitCounters) return false;
-  const grid::StreamPlan p = grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost);
+  const grid::StreamPlan p = stream_plan_for(bh, Sq, stream_off(Sq, kv));
   return p.ok && p.units >= (long long)kStreamMinShare * kStreamMaxGroups;
 }
-grid::StreamPlan stream_plan_for(long long bh, int Sq) {
-  return grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost);
+size_t split_workspace_bytes(long long bh, int Sq, int D, const KvSpec& kv) {
+  const grid::StreamPlan p = stream_plan_for(bh, Sq, stream_off(Sq, kv));
+  // per slot: BM x D fp16 values, then BM x 4 floats
+  return kSplitCounterBytes + 2 * (size_t)p.G * kStreamBM * (sizeof(uint16_t) * (size_t)D + 4 * sizeof(float));
 }
 }  // namespace
 
 size_t prefill_split_workspace_bytes(int B, int Sq, int Hq, int D, bool causal) {
   const long long bh = (long long)B * Hq;
   const KvSpec kv{};
-  if (!split_applies(bh, Sq, causal, kv)) return 0;
-  const grid::StreamPlan p = stream_plan_for(bh, Sq);
-  // per slot: BM x D fp16 values, then BM x 4 floats
-  return kSplitCounterBytes + 2 * (size_t)p.G * kStreamBM * (sizeof(uint16_t) * (size_t)D + 4 * sizeof(float));
+  return split_applies(bh, Sq, causal, kv) ? split_workspace_bytes(bh, Sq, D, kv) : 0;
+}
+
+size_t prefill_cache_split_workspace_bytes(int B, int Sq, int Hq, int D, int max_kv, bool causal, int window) {
+  const long long bh = (long long)B * Hq;
+  static const int32_t probe = 0;  // stands for the per-sequence lengths: only its presence matters here
+  KvSpec kv{};
+  kv.lens = &probe;
+  kv.max_kv = max_kv;
+  kv.window = window;
+  return split_applies(bh, Sq, causal, kv) ? split_workspace_bytes(bh, Sq, D, kv) : 0;
 }
 
 hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v, void* out, int B, int Sq, int Hq,
@@ -859,7 +884,8 @@ hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v
   if (!ws || !split_applies(bh, Sq, causal, kv))
     return launch_prefill_bf16(q, k, v, out, B, Sq, Hq, Hkv, D, causal, scale, kv, nullptr, st);
   const float c_log2 = (float)((double)scale * 1.4426950408889634);
-  const grid::StreamPlan p = stream_plan_for(bh, Sq);
+  const int off = stream_off(Sq, kv);
+  const grid::StreamPlan p = stream_plan_for(bh, Sq, off);
   const size_t nslots = 2 * (size_t)p.G;
   SplitArgs sa;
   sa.cnt = reinterpret_cast<int*>(ws);
@@ -870,19 +896,22 @@ hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v
   sa.tile_cost = p.tile_cost;
   for (int j = 0, s = 0; j <= p.nqt; j++) {
     sa.tstart[j] = s;
-    if (j < p.nqt) s += grid::stream_ntiles(Sq, grid::stream_pair_qt(j, p.nqt), kStreamBM);
+    if (j < p.nqt) s += grid::stream_ntiles(Sq, grid::stream_pair_qt(j, p.nqt), kStreamBM, off);
   }
   for (int w = 0; w <= p.G; w++)
-    sa.wstart[w] = grid::stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, kStreamBM, p.tile_cost);
+    sa.wstart[w] = grid::stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, kStreamBM, p.tile_cost, off);
   const dim3 grid((unsigned)p.G), block(512);
-  if (D == 64)
-    hipLaunchKernelGGL((prefill_bf16_kernel<64, 8, false, 1, 64, false, true>), grid, block, 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, 1, c_log2, p.nqt, p.nqt, kv, nullptr,
-                       sa);
-  else
-    hipLaunchKernelGGL((prefill_bf16_kernel<128, 8, false, 1, 64, false, true>), grid, block, 0, st, (const bf16*)q,
-                       (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, 1, c_log2, p.nqt, p.nqt, kv, nullptr,
-                       sa);
+#define RCGQA_SPLIT_LAUNCH(DD, GG)                                                                                   \
+  hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, GG, 1, 64, false, true>), grid, block, 0, st, (const bf16*)q,     \
+                     (const bf16*)k, (const bf16*)v, (bf16*)out, Sq, Hq, Hkv, 1, c_log2, p.nqt, p.nqt, kv, nullptr, sa)
+  if (kv.lens) {
+    if (D == 64) RCGQA_SPLIT_LAUNCH(64, true);
+    else RCGQA_SPLIT_LAUNCH(128, true);
+  } else {
+    if (D == 64) RCGQA_SPLIT_LAUNCH(64, false);
+    else RCGQA_SPLIT_LAUNCH(128, false);
+  }
+#undef RCGQA_SPLIT_LAUNCH
   return hipGetLastError();
 }
 

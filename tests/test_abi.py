@@ -109,6 +109,46 @@ def test_prefill_cache_rejects(args):
     assert st == BD.EINVAL
 
 
+def test_prefill_cache_workspace_bytes():
+    L = R.lib()
+    # a chunk of 512 new tokens after 4096 cached ones, 16 heads x 2 sequences: stream-K, 256 workgroups
+    assert L.attn_prefill_cache_workspace_bytes(2, 512, 16, 128, 4608, 1, 0) == 4096 + 256 * 2 * 256 * (2 * 128 + 16)
+    assert L.attn_prefill_cache_workspace_bytes(2, 512, 16, 128, 4608, 1, 1024) == 0   # windowed
+    assert L.attn_prefill_cache_workspace_bytes(2, 512, 16, 128, 4608, 1, 4608) > 0    # a window of max_kv is none
+    assert L.attn_prefill_cache_workspace_bytes(2, 512, 16, 128, 4608, 0, 0) == 0      # not causal
+    assert L.attn_prefill_cache_workspace_bytes(2, 512, 16, 128, 400, 1, 0) == 0       # cache shorter than the chunk
+    assert L.attn_prefill_cache_workspace_bytes(2, 512, 32, 128, 4608, 1, 0) == 0      # the key-group grid is full
+    assert L.attn_prefill_cache_workspace_bytes(64, 512, 32, 128, 4608, 1, 0) == 0     # paired grid
+    assert L.attn_prefill_cache_workspace_bytes(1, 512, 8, 128, 4096, 1, 0) == 0       # too little work
+    assert L.attn_prefill_cache_workspace_bytes(0, 512, 8, 128, 4096, 1, 0) == 0
+    assert L.attn_prefill_cache_workspace_bytes(2, 512, 16, 128, 4608, 1, -1) == 0
+    # a chunk that is the whole sequence plans as the plain prefill
+    assert L.attn_prefill_cache_workspace_bytes(1, 8192, 2, 128, 8192, 1, 0) == L.attn_prefill_workspace_bytes(1, 8192, 2, 128, 1) > 0
+
+
+@pytest.mark.parametrize("args", [
+    dict(ws=None), dict(wbytes=100), dict(ws_addr=4096 * 64 + 64), dict(ws_is="out"), dict(ws_is="lens"),
+    dict(lens=None), dict(Hq=6, Hkv=4), dict(window=-1), dict(window=8, causal=0), dict(max_kv=0), dict(causal=2),
+    dict(scale=0.0), dict(dt=3),
+])
+def test_prefill_cache_ws_rejects(args):
+    a = dict(B=2, Sq=512, Hq=16, Hkv=16, D=128, max_kv=4608, causal=1, window=0, scale=0.1, dt=0, ws_addr=4096 * 64,
+             wbytes=1 << 30, lens=A[4])
+    a.update(args)
+    q, kc, vc, out = A[0], A[1], A[2], A[3]
+    ws = ctypes.c_void_p(a["ws_addr"])
+    if "ws" in args:
+        ws = None
+    elif args.get("ws_is") == "out":
+        ws = out
+    elif args.get("ws_is") == "lens":
+        ws = a["lens"]
+    st = R.lib().attn_prefill_cache_ws(q, kc, vc, a["lens"], out, a["B"], a["Sq"], a["Hq"], a["Hkv"], a["D"],
+                                       a["max_kv"], a["causal"], a["window"], a["scale"], a["dt"], ws, a["wbytes"],
+                                       None)
+    assert st == BD.EINVAL
+
+
 def test_prefill_cache_unsupported_head_dim():
     assert R.lib().attn_prefill_cache(FAKE, FAKE, FAKE, FAKE, ctypes.c_void_p(8192), 1, 4, 8, 2, 96, 10, 1, 0, 0.1,
                                       0, None) == BD.EUNSUPPORTED
@@ -220,6 +260,8 @@ WS = ctypes.c_void_p(4096 * 64)
     lambda L: L.attn_prefill_cache(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 16, 1, 0, 0.125, 0, None),
     lambda L: L.attn_prefill_masked(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 1, 4, 1, 0.125, 0, None),
     lambda L: L.attn_prefill_ws(A[0], MIS, A[2], A[3], 1, 4, 8, 2, 64, 1, 0.125, 0, WS, 1 << 20, None),
+    lambda L: L.attn_prefill_cache_ws(A[0], A[1], A[2], MIS, A[4], 1, 4, 8, 2, 64, 16, 1, 0, 0.125, 0, WS, 1 << 20,
+                                      None),
     lambda L: L.attn_decode(A[0], MIS, A[2], A[3], A[4], 1, 8, 2, 128, 16, 0.1, 0, WS, 1 << 30, None),
     lambda L: L.rope_attn_prefill(A[0], A[1], A[2], MIS, None, 1, 16, 8, 2, 64, 1, 0.125, 1e4, 1.0, 0, WS, 1 << 20,
                                   None),

@@ -30,22 +30,22 @@ int main() {
       std::vector<double> w(k);
       for (auto& x : w) std::scanf("%lf", &x);
       std::printf("%.3f\n", busiest_cu(w, bh));
-    } else if (what[0] == 's') {                // stream bh Sq BM min_units tile_cost: plan, then every piece
-      long long bh; int Sq, BM, mu, tc;
-      std::scanf("%lld %d %d %d %d", &bh, &Sq, &BM, &mu, &tc);
-      const StreamPlan p = stream_plan(bh, Sq, BM, kCUs, mu, tc);
+    } else if (what[0] == 's') {                // stream bh Sq BM min_units tile_cost off: plan, then every piece
+      long long bh; int Sq, BM, mu, tc, off;
+      std::scanf("%lld %d %d %d %d %d", &bh, &Sq, &BM, &mu, &tc, &off);
+      const StreamPlan p = stream_plan(bh, Sq, BM, kCUs, mu, tc, off);
       std::printf("%d %d %d %d %d\n", p.nqt, p.units, p.G, p.cost, p.ok ? 1 : 0);
       for (int w = 0; w < p.G; w++) {   // the kernel's walk over its range
-        const int a = stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
-        const int e = stream_start(w + 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
+        const int a = stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
+        const int e = stream_start(w + 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
         for (int u = a; u < e;) {
-          const StreamTile t = stream_tile(u, p.nqt, p.per, Sq, BM);
+          const StreamTile t = stream_tile(u, p.nqt, p.per, Sq, BM, off);
           const int k_hi = std::min(t.n, t.k + (e - u));
-          const int w0 = stream_owner(t.t0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
-          const int w1 = stream_owner(t.t0 + t.n - 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc);
+          const int w0 = stream_owner(t.t0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
+          const int w1 = stream_owner(t.t0 + t.n - 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
           const long long me = 2LL * w + (t.t0 > a ? 1 : 0);
           const long long s0 =
-              2LL * w0 + (t.t0 > stream_start(w0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc) ? 1 : 0);
+              2LL * w0 + (t.t0 > stream_start(w0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off) ? 1 : 0);
           std::printf("%d %d %d %d %d %d %d %d %lld %d %d %lld %d %d\n", w, t.bh, t.qt, t.k, k_hi, t.n, t.t0,
                       t.tile, w1 > w0 ? me : -1LL, w0, w1, s0, a, e);
           u += k_hi - t.k;
@@ -142,12 +142,15 @@ def test_grid_choice_on_timed_shapes(model, shape, four):
     assert int(got[1]) == (((nqt2 + 1) // 2 if paired else nqt2) if four else nqt4)
 
 
-@pytest.mark.parametrize("bh,Sq,BM,mu,tc", [(8, 4096, 256, 4, 3), (8, 2100, 256, 4, 3), (1, 1, 256, 4, 3),
-                                             (1, 257, 256, 4, 3), (4, 8192, 256, 4, 3), (16, 300, 256, 4, 3),
-                                             (2, 64, 256, 1, 0), (8, 1024, 128, 4, 2), (3, 5000, 256, 7, 5),
-                                             (64, 4096, 256, 4, 3)])
-def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc):
-    """The stream-K grid (small causal problems): workgroups take contiguous,
+@pytest.mark.parametrize("bh,Sq,BM,mu,tc,off", [(8, 4096, 256, 4, 3, 0), (8, 2100, 256, 4, 3, 0), (1, 1, 256, 4, 3, 0),
+                                                 (1, 257, 256, 4, 3, 0), (4, 8192, 256, 4, 3, 0),
+                                                 (16, 300, 256, 4, 3, 0), (2, 64, 256, 1, 0, 0),
+                                                 (8, 1024, 128, 4, 2, 0), (3, 5000, 256, 7, 5, 0),
+                                                 (64, 4096, 256, 4, 3, 0), (64, 512, 256, 4, 2, 4096),
+                                                 (8, 700, 256, 4, 2, 3000), (3, 1, 256, 4, 2, 77)])
+def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc, off):
+    """The stream-K grid (causal problems on unpaired grids, plain or against a
+    cache of `off` earlier tokens): workgroups take contiguous,
     non-empty ranges of the unit list (batch-head, then query tiles in heavy /
     light pairs, then key tile) that balance units plus tc per tile started;
     the pieces cover every key tile a query tile sees under the causal rule
@@ -155,11 +158,12 @@ def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc):
     distinct partial slot (at most two per workgroup, the first piece of a
     range in slot 2w, the last in 2w + 1), and the merge order (workgroups
     w0..w1, slot s0 for w0 and 2w after) is the key order."""
-    out = model([f"s {bh} {Sq} {BM} {mu} {tc}"])
+    out = model([f"s {bh} {Sq} {BM} {mu} {tc} {off}"])
     nqt, units, G, cost, ok = (int(x) for x in out[0].split())
     assert ok == (cost * (G + 1) < 2 ** 31) and ok
     rows = [tuple(int(x) for x in r.split()) for r in out[1:]]
-    ntiles = [(min(Sq, BM * (qt + 1)) + 63) // 64 for qt in range(nqt)]
+    # query row i at key position i + off: tile qt sees keys below min(Sq, BM (qt + 1)) + off
+    ntiles = [(min(Sq, BM * (qt + 1)) + off + 63) // 64 for qt in range(nqt)]
     assert nqt == -(-Sq // BM) and units == bh * sum(ntiles) and cost == units + tc * bh * nqt
     assert G == max(1, min(256, units // max(mu, tc + 2)))
     # list order: (batch, head), then query tiles in heavy / light pairs

@@ -20,7 +20,8 @@ timed steps; `gqa_prefill` times attn_prefill on the LLaMA-70B-shaped GQA
 prefill (B=1 S=4096 Hq=64 Hkv=8 D=128) and, on its 8-query-head / 1-KV-head
 share, the stream-K entry point attn_prefill_ws (attn_prefill alongside);
 `stream_k_prefill` times attn_prefill_ws against attn_prefill on four more causal
-shapes that the launcher runs on unpaired grids; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
+shapes that the launcher runs on unpaired grids, and attn_prefill_cache_ws against
+attn_prefill_cache on two chunked prefills; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
 entry points against the separate calls on the same workloads; `ntk_rope`
 times rope_apply at an NTK-aware scaled base; `masked_prefill` times
 attn_prefill_masked (causal plus a key-padding mask) on LLaMA-7B-shaped heads.  `cpu_baseline` times the float64 oracle on a bounded sample on
@@ -243,6 +244,26 @@ def _next_rows(R, dev, stream):
                      "attn_prefill_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
                      "speedup": round(ms / ws_ms, 3)})
         del q, k, v, o, wsp
+    # and attn_prefill_cache_ws against attn_prefill_cache on chunks whose key-group grid underfills the GPU
+    for B, Sq, Hq, Hkv, L in ((1, 2048, 8, 1, 8192), (2, 512, 16, 2, 16384)):
+        D = 128
+        q = torch.randn((B, Sq, Hq, D), generator=g, device=dev).to(torch.bfloat16)
+        kc = torch.randn((B, Hkv, L, D), generator=g, device=dev).to(torch.bfloat16)
+        vc = torch.randn((B, Hkv, L, D), generator=g, device=dev).to(torch.bfloat16)
+        lens = torch.full((B,), L, dtype=torch.int32, device=dev)
+        o = torch.empty_like(q)
+        wsp = torch.zeros(max(R.attn_prefill_cache_workspace_bytes(B, Sq, Hq, D, L, True, 0), 1), dtype=torch.uint8,
+                          device=dev)
+        ws_ms = _time_launches(lambda: R.attn_prefill_cache_ws(q, kc, vc, lens, o, causal=True, scale=D ** -0.5,
+                                                               workspace=wsp), stream)
+        ms = _time_launches(lambda: R.attn_prefill_cache(q, kc, vc, lens, o, causal=True, scale=D ** -0.5), stream)
+        flops = 4.0 * D * Hq * B * sum(L - Sq + i + 1 for i in range(Sq))
+        rows.append({"workload": f"B={B} Sq={Sq} new tokens after {L - Sq} cached, Hq={Hq} Hkv={Hkv} D={D} bf16 causal",
+                     "attn_prefill_cache_ws_ms": round(ws_ms, 4), "attn_prefill_cache_ms": round(ms, 4),
+                     "attn_prefill_cache_ws_tflops": round(flops / (ws_ms * 1e-3) / 1e12, 2),
+                     "attn_prefill_cache_tflops": round(flops / (ms * 1e-3) / 1e12, 2),
+                     "speedup": round(ms / ws_ms, 3)})
+        del q, kc, vc, o, wsp
     out["stream_k_prefill"] = rows
     return out
 

@@ -22,6 +22,8 @@
 // loads it, with the very same values and arithmetic), and a second kernel
 // rotates a decode step's q and new key and appends the key and value to the
 // cache in one launch.
+#include <algorithm>
+
 #include "common.h"
 #include "launch.h"
 
@@ -30,6 +32,7 @@ namespace rcgqa {
 // Largest grid of the per-token kernels: 2^20 workgroups of 256 work-items
 // keep the launch far inside the 32-bit work-item count of a dispatch.
 constexpr int kMaxTokenGroups = 1 << 20;
+constexpr int kMinTokenGroups = 2048;
 
 template <typename T, int VE>
 struct alignas(sizeof(T) * VE) Vec {
@@ -68,26 +71,43 @@ __device__ __forceinline__ void rope_pair(const T* s1, const T* s2, T* d1, T* d2
 
 // q may be null with Hq == 0 (keys only); table, when not null, receives the
 // token's cos/sin row: table[tok * D + i] = cos, table[tok * D + D/2 + i] = sin.
+// A workgroup takes tpi consecutive tokens at a time (tpi * D/2 <= 256 when
+// tpi > 1): the inverse frequencies are formed once per workgroup, the tpi
+// tokens' angles are spread over its threads, then their q/k vectors are
+// rotated.  The angles and arithmetic do not depend on tpi.
 template <typename T, int VE>
 __global__ __launch_bounds__(256) void rope_kernel(T* __restrict__ q, T* __restrict__ k,
                                                    const int32_t* __restrict__ pos_ids, long long ntok, int S,
                                                    int Hq, int Hkv, int D, double theta, double factor,
-                                                   float* __restrict__ table) {
-  extern __shared__ float cs[];  // cos[D/2] then sin[D/2]
+                                                   float* __restrict__ table, int tpi) {
+  extern __shared__ float cs[];  // tpi rows of cos[D/2] then sin[D/2], then the inverse frequencies (double)
   const int half = D >> 1;
+  double* const inv = reinterpret_cast<double*>(cs + (size_t)tpi * D);
+  for (int i = threadIdx.x; i < half; i += blockDim.x) inv[i] = pow(theta, -2.0 * (double)i / (double)D);
   const int cpr = half / VE;  // vectors per half head-vector
   const int units = (Hq + Hkv) * cpr;
-  for (long long tok = blockIdx.x; tok < ntok; tok += gridDim.x) {
-    if (tok != (long long)blockIdx.x) __syncthreads();  // the previous token's cs fully read
-    const int pos = pos_ids ? pos_ids[tok] : (int)(tok % S);
-    rope_angles(cs, pos, D, theta, factor);
+  for (long long t0 = (long long)blockIdx.x * tpi; t0 < ntok; t0 += (long long)gridDim.x * tpi) {
+    __syncthreads();  // inv written / the previous tokens' cs fully read
+    const int nt = ntok - t0 < tpi ? (int)(ntok - t0) : tpi;
+    for (int j = threadIdx.x; j < nt * half; j += blockDim.x) {
+      const int tt = j / half, i = j - tt * half;
+      const long long tok = t0 + tt;
+      const int pos = pos_ids ? pos_ids[tok] : (int)(tok % S);
+      const double a = ((double)pos / factor) * inv[i];
+      double sn, cn;
+      sincos(a, &sn, &cn);
+      cs[tt * D + i] = (float)cn;
+      cs[tt * D + half + i] = (float)sn;
+    }
     __syncthreads();
     if (table)
-      for (int i = threadIdx.x; i < D; i += blockDim.x) table[(size_t)tok * D + i] = cs[i];
-    for (int u = threadIdx.x; u < units; u += blockDim.x) {
-      const int head = u / cpr, c = u - head * cpr;
+      for (int j = threadIdx.x; j < nt * D; j += blockDim.x) table[(size_t)t0 * D + j] = cs[j];
+    for (int u = threadIdx.x; u < nt * units; u += blockDim.x) {
+      const int tt = u / units, r = u - tt * units;
+      const int head = r / cpr, c = r - head * cpr;
+      const long long tok = t0 + tt;
       T* base = head < Hq ? q + ((size_t)tok * Hq + head) * D : k + ((size_t)tok * Hkv + (head - Hq)) * D;
-      rope_pair<T, VE>(base + c * VE, base + half + c * VE, base + c * VE, base + half + c * VE, cs, c, half);
+      rope_pair<T, VE>(base + c * VE, base + half + c * VE, base + c * VE, base + half + c * VE, cs + tt * D, c, half);
     }
   }
 }
@@ -170,23 +190,28 @@ __global__ __launch_bounds__(256) void rope_append_kernel(const T* __restrict__ 
 hipError_t launch_rope(void* q, void* k, const int32_t* pos, int B, int S, int Hq, int Hkv, int D,
                        double theta, double factor, bool bf16_io, float* table, hipStream_t st) {
   const long long ntok = (long long)B * S;
-  const dim3 grid((unsigned)(ntok < kMaxTokenGroups ? ntok : kMaxTokenGroups)), block(256);
-  const size_t lds = (size_t)D * sizeof(float);
   const int half = D / 2;
+  // Several tokens per workgroup only while the grid keeps at least
+  // kMinTokenGroups workgroups (8 per CU); short launches keep one token each.
+  const long long fill = ntok / kMinTokenGroups;
+  const int tpi = (int)std::max(1LL, std::min(fill, (long long)(half <= 256 ? 256 / half : 1)));
+  const long long groups = (ntok + tpi - 1) / tpi;
+  const dim3 grid((unsigned)(groups < kMaxTokenGroups ? groups : kMaxTokenGroups)), block(256);
+  const size_t lds = (size_t)tpi * D * sizeof(float) + (size_t)half * sizeof(double);
   if (bf16_io) {
     if (half % 8 == 0)
       hipLaunchKernelGGL((rope_kernel<bf16, 8>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, ntok, S, Hq, Hkv, D,
-                         theta, factor, table);
+                         theta, factor, table, tpi);
     else
       hipLaunchKernelGGL((rope_kernel<bf16, 1>), grid, block, lds, st, (bf16*)q, (bf16*)k, pos, ntok, S, Hq, Hkv, D,
-                         theta, factor, table);
+                         theta, factor, table, tpi);
   } else {
     if (half % 4 == 0)
       hipLaunchKernelGGL((rope_kernel<float, 4>), grid, block, lds, st, (float*)q, (float*)k, pos, ntok, S, Hq, Hkv,
-                         D, theta, factor, table);
+                         D, theta, factor, table, tpi);
     else
       hipLaunchKernelGGL((rope_kernel<float, 1>), grid, block, lds, st, (float*)q, (float*)k, pos, ntok, S, Hq, Hkv,
-                         D, theta, factor, table);
+                         D, theta, factor, table, tpi);
   }
   return hipGetLastError();
 }

@@ -54,6 +54,18 @@ def test_rope_head_dims(dtype, D):
     _run(q, k, pos, 500000.0, 4.0, dtype, f"rope D={D} {dtype} random positions")
 
 
+@pytest.mark.parametrize("dtype", ["fp32", "bf16"])
+@pytest.mark.parametrize("D", [6, 64, 256])
+def test_rope_several_tokens_per_workgroup(dtype, D):
+    """9003 tokens: workgroups take 4 tokens at a time (2 at D=256), the last
+    one a ragged 3 (1); random positions, every element against the oracle."""
+    B, S, Hq, Hkv = 3, 3001, 2, 1
+    q = W.random_case(300 + D, (B, S, Hq, D), dtype)
+    k = W.random_case(301 + D, (B, S, Hkv, D), dtype)
+    pos = np.random.Generator(np.random.PCG64(302 + D)).integers(0, 1 << 16, size=(B, S)).astype(np.int32)
+    _run(q, k, pos, 10000.0, 1.0, dtype, f"rope D={D} {dtype} {B * S} tokens, several per workgroup")
+
+
 def test_rope_fp32_long_positions():
     # the fp32 bound must hold far from position 0 as well
     q = W.random_case(5, (1, 8, 2, 128), "fp32")
@@ -123,9 +135,11 @@ def test_rope_ntk_scaled_base(dtype):
 
 @pytest.mark.parametrize("style", ["half", "interleaved"])
 def test_rope_more_tokens_than_workgroups(style):
-    """2^20 + 74 tokens: the grid stops at 2^20 workgroups, so the last 74
-    tokens are a second token of the first 74 workgroups.  Checked on those
-    tokens, their neighbours and a sample of the rest, at default positions."""
+    """2^20 + 74 tokens.  Interleaved pairs: the grid stops at 2^20
+    workgroups, so the last 74 tokens are a second token of the first 74
+    workgroups.  Half pairs: workgroups take 64 tokens at a time (D=8), the
+    last one a ragged 10.  Checked on the last tokens and a sample of the
+    rest, at default positions."""
     import torch
     B, S, Hq, Hkv, D = 2, (1 << 19) + 37, 2, 1, 8
     announce(f"rope {style} {B * S} tokens (grid-stride)")

@@ -85,22 +85,14 @@ inline KeyGroupGrid key_group_grid(long long bh, int Sq, bool causal, long long 
   return {four, four ? npairs2 : nqt4};
 }
 
-// Stream-K plan for small causal grids (no cache, no mask).  A unit is one
-// (query tile of BM rows, 64-key tile) step of the causal work.  Units are
-// listed (batch, head) by (batch, head); within one, query tiles in heavy /
-// light pairs (the last tile, the first, the second last, the second, ...),
-// and within a tile key tile by key tile.  Each workgroup takes a contiguous
-// range of the list.  The ranges balance a cost of one per unit plus
-// `tile_cost` per tile started (the prologue and the hand-over a piece of a
-// tile brings), through the cumulative cost C(u) = u + tile_cost * (tiles
-// that start before unit u): workgroup w starts at the first unit u with
-// C(u) G >= w C(units).  A query tile whose units fall to several
-// workgroups is finished by merging their partial softmax states; each
-// workgroup has at most two such pieces (the first and the last of its
-// range), kept in slots 2 w and 2 w + 1.  All in 32-bit integers (the plan
-// is used only where C(units) G fits), constexpr so that the kernel runs
-// this code: every (batch, head) block has the same layout, so each step is
-// one division and a walk over one block's tiles.
+// Stream-K plan for small causal grids.  A unit is one (query tile of BM
+// rows, 64-key tile) step of the causal work.  Units are listed (batch, head)
+// by (batch, head); within one, query tiles in heavy / light pairs (the last
+// tile, the first, the second last, the second, ...), and within a tile key
+// tile by key tile.  Each workgroup takes a contiguous range of the list.  A
+// query tile whose units fall to several workgroups is finished by merging
+// their partial softmax states; each workgroup has at most two such pieces
+// (the first and the last of its range), kept in slots 2 w and 2 w + 1.
 // Key tiles that query tile qt sees when query row i sits at key position
 // i + off (off = keys before the first query row: 0 for a plain prefill, the
 // cached tokens before the chunk for a prefill against a cache).
@@ -111,78 +103,114 @@ constexpr int stream_ntiles(int Sq, int qt, int BM, int off = 0) {
 constexpr int stream_pair_qt(int j, int nqt) { return (j & 1) ? (j >> 1) : nqt - 1 - (j >> 1); }
 
 struct StreamPlan {
-  int nqt;        // query tiles per (batch, head)
-  int per;        // units per (batch, head)
-  int units;      // all units
-  int G;          // workgroups
-  int tile_cost;  // cost of starting a tile, in units
-  int cost;       // C(units)
-  bool ok;        // the sizes fit the 32-bit arithmetic
+  int nqt;         // query tiles per (batch, head)
+  int per;         // units per (batch, head)
+  int units;       // all units
+  int G;           // workgroups
+  int piece_cost;  // cost of a piece (its prologue), in units
+  bool ok;         // the sizes fit the 32-bit arithmetic
 };
 
-inline StreamPlan stream_plan(long long bh, int Sq, int BM, int slots, int min_units, int tile_cost, int off = 0) {
+inline StreamPlan stream_plan(long long bh, int Sq, int BM, int slots, int min_units, int piece_cost, int off = 0) {
   const int nqt = (Sq + BM - 1) / BM;
   long long per = 0;
   for (int qt = 0; qt < nqt; qt++) per += stream_ntiles(Sq, qt, BM, off);
-  const long long units = bh * per, cost = units + (long long)tile_cost * bh * nqt;
-  // at least min_units units and more than tile_cost + 1 of cost per workgroup, so that no range is empty
+  const long long units = bh * per, cost = units + (long long)piece_cost * bh * nqt;
+  // at least min_units units and more than piece_cost + 1 of cost per workgroup
   const long long G =
-      std::max<long long>(1, std::min<long long>(slots, units / std::max(min_units, tile_cost + 2)));
-  const bool ok = cost * (G + 1) < (1LL << 31);
-  return {nqt, (int)per, (int)units, (int)G, tile_cost, (int)cost, ok};
+      std::max<long long>(1, std::min<long long>(slots, units / std::max(min_units, piece_cost + 2)));
+  const bool ok = cost + G < (1LL << 31);
+  return {nqt, (int)per, (int)units, (int)G, piece_cost, ok};
 }
 
-// The query tile that unit u falls in: its (batch, head), query tile qt, key
-// tile k within it, its key-tile count n, its first unit t0, its counter
-// slot (bh nqt + qt) and the number of tiles that start before it.
-struct StreamTile {
-  int bh, qt, k, n, t0, tile, before;
+// The workgroups' ranges, computed on the host.  A range costs one per unit,
+// plus piece_cost per query tile it touches (each piece loads its query rows
+// and first K/V tile), plus merge_cost when it ends inside a tile: it then
+// holds that tile's first pieces, runs them last and completes the tile's
+// count, so it merges the pieces.  The ranges are the greedy cover (each
+// workgroup takes the longest range within a budget) under the least budget
+// that needs at most G workgroups; trailing workgroups may be left empty.
+// For each workgroup: its first unit (wstart[G] = units), the list index of
+// the tile holding its first unit, the workgroup holding that tile's first
+// unit (lo_owner) and the one holding the last unit of the tile its range
+// ends in (hi_owner): a tile shared by workgroups w0..w1 has one piece in
+// each of them.
+struct StreamRanges {
+  std::vector<int> wstart, first_tile, lo_owner, hi_owner;
+  long long budget;
 };
-constexpr StreamTile stream_tile(int u, int nqt, int per, int Sq, int BM, int off = 0) {
-  const int b = u / per, r = u - b * per;
-  int s = 0, j = 0;
-  for (; j < nqt - 1; j++) {
-    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM, off);
-    if (r < s + n) break;
-    s += n;
-  }
-  const int qt = stream_pair_qt(j, nqt);
-  return {b, qt, r - s, stream_ntiles(Sq, qt, BM, off), b * per + s, b * nqt + qt, b * nqt + j};
-}
 
-// C(u) for 0 <= u <= units
-constexpr int stream_cost(int u, int units, int nqt, int per, int Sq, int BM, int tile_cost, int off = 0) {
-  if (u >= units) return units + tile_cost * (units / per) * nqt;
-  const StreamTile t = stream_tile(u, nqt, per, Sq, BM, off);
-  return u + tile_cost * (t.before + (u > t.t0 ? 1 : 0));
-}
-
-// First unit of workgroup w (w = G gives `units`): the first u with
-// C(u) >= c = ceil(w cost / G), found in the (batch, head) block that c
-// falls in (each block adds per + tile_cost nqt to C)
-constexpr int stream_start(int w, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost,
-                           int off = 0) {
-  const int c = (w * cost + G - 1) / G;
-  const int cb = per + tile_cost * nqt;
-  const int b = c / cb, rem = c - b * cb;
-  if (b * per >= units) return units;
-  int s = 0;
-  for (int j = 0; j < nqt; j++) {
-    if (rem <= s + tile_cost * j) return b * per + s;  // at tile j's first unit
-    const int n = stream_ntiles(Sq, stream_pair_qt(j, nqt), BM, off);
-    if (rem <= s + n + tile_cost * (j + 1)) {           // inside tile j: C = u + tile_cost (j + 1)
-      const int r = rem - tile_cost * (j + 1);
-      return b * per + (r > s + 1 ? r : s + 1);
+// Workgroups the greedy cover under `budget` takes (G + 1: more than G);
+// fills ws[0..G] when given.  tst[j]: first unit of list tile j within its
+// (batch, head) block, tst[nqt] = per.
+inline int stream_cover(const std::vector<int>& tst, int nqt, int per, int units, int G, int piece_cost,
+                        int merge_cost, long long budget, int* ws) {
+  int w = 0, ti = 0;  // ti: list index of the tile holding unit u
+  long long u = 0;
+  while (u < units) {
+    if (w == G) return G + 1;
+    if (ws) ws[w] = (int)u;
+    const long long a = u;
+    long long cost = 0;
+    for (;;) {
+      const int b = ti / nqt, j = ti - b * nqt;
+      const long long end = (long long)b * per + tst[j + 1];
+      const long long whole = cost + piece_cost + (end - u);
+      if (whole <= budget) {  // the rest of this tile
+        cost = whole;
+        u = end;
+        ti++;
+        if (u == units) break;
+        continue;
+      }
+      const long long k = budget - cost - piece_cost - merge_cost;  // a part of it, ending inside it
+      if (k >= 1) u += std::min(k, end - u - 1);
+      else if (u == a) return G + 1;  // not even one unit fits this budget
+      break;
     }
-    s += n;
+    w++;
   }
-  return b * per + per;
+  if (ws)
+    for (int x = w; x <= G; x++) ws[x] = units;
+  return w;
 }
 
-// Workgroup that runs unit u (u < units)
-constexpr int stream_owner(int u, int G, int units, int cost, int nqt, int per, int Sq, int BM, int tile_cost,
-                           int off = 0) {
-  return stream_cost(u, units, nqt, per, Sq, BM, tile_cost, off) * G / cost;
+inline StreamRanges stream_ranges(const StreamPlan& p, long long bh, int Sq, int BM, int merge_cost, int off = 0) {
+  std::vector<int> tst(p.nqt + 1, 0);
+  for (int j = 0; j < p.nqt; j++) tst[j + 1] = tst[j] + stream_ntiles(Sq, stream_pair_qt(j, p.nqt), BM, off);
+  long long lo = 0, hi = (long long)p.units + (long long)p.piece_cost * bh * p.nqt + merge_cost;  // hi always fits
+  while (lo < hi) {
+    const long long mid = (lo + hi) / 2;
+    if (stream_cover(tst, p.nqt, p.per, p.units, p.G, p.piece_cost, merge_cost, mid, nullptr) <= p.G) hi = mid;
+    else lo = mid + 1;
+  }
+  StreamRanges r;
+  r.budget = hi;
+  r.wstart.assign(p.G + 1, 0);
+  stream_cover(tst, p.nqt, p.per, p.units, p.G, p.piece_cost, merge_cost, hi, r.wstart.data());
+  r.first_tile.assign(p.G, 0);
+  r.lo_owner.assign(p.G, 0);
+  r.hi_owner.assign(p.G, 0);
+  // list index and first unit of the tile holding unit u
+  auto tile_of = [&](int u) {
+    const int b = u / p.per, rr = u - b * p.per;
+    const int j = (int)(std::upper_bound(tst.begin(), tst.begin() + p.nqt, rr) - tst.begin()) - 1;
+    return std::make_pair(b * p.nqt + j, b * p.per + tst[j]);
+  };
+  auto owner = [&](int u) {  // the non-empty range holding u
+    return (int)(std::upper_bound(r.wstart.begin(), r.wstart.end(), u) - r.wstart.begin()) - 1;
+  };
+  for (int w = 0; w < p.G; w++) {
+    const int a = r.wstart[w], e = r.wstart[w + 1];
+    if (a >= e) continue;
+    const auto first = tile_of(a);
+    r.first_tile[w] = first.first;
+    r.lo_owner[w] = owner(first.second);
+    const auto last = tile_of(e - 1);
+    const int lb = last.first / p.nqt, lj = last.first - lb * p.nqt;
+    r.hi_owner[w] = owner(lb * p.per + tst[lj + 1] - 1);
+  }
+  return r;
 }
 
 }  // namespace grid

@@ -91,23 +91,27 @@ __device__ __forceinline__ void lds_buf16(const void* base, uint32_t voff, bf16*
                "s"(m));
 }
 
-// Stream-K state of one launch (SPL kernels only; see grid::stream_plan):
+// Stream-K state of one launch (SPL kernels only; see grid::stream_ranges):
 // one counter per query tile at cnt, partial O blocks of BM x D fp16 values
 // at o (pairs packed in 32-bit words, in the accumulator layout: [wave]
 // [register pair][lane]), the (reference max, row sum, O scale, unused)
-// rows [slot][BM][4] at ml; the plan's units
-// per (batch, head), total cost and cost per tile start; the first unit of
-// every query tile of a (batch, head) block in list order (tstart[nqt] =
-// per) and of every workgroup (wstart[G] = all units), computed on the host.
+// rows [slot][BM][4] at ml; the plan's units per (batch, head); the first
+// unit of every query tile of a (batch, head) block in list order
+// (tstart[nqt] = per) and of every workgroup (wstart[G] = all units); per
+// workgroup the list index of the tile holding its first unit, the
+// workgroup holding that tile's first unit and the one holding the last
+// unit of the tile its range ends in.  All computed on the host.
 constexpr int kStreamMaxTiles = 128;  // query tiles per (batch, head): S up to 32768
 constexpr int kStreamMaxGroups = 256;
 struct SplitArgs {
   uint32_t* o;
   float* ml;
   int* cnt;
-  int per, cost, tile_cost;
+  int per;
   int tstart[kStreamMaxTiles + 1];
   int wstart[kStreamMaxGroups + 1];
+  uint16_t wtile[kStreamMaxGroups];
+  uint8_t wlo[kStreamMaxGroups], whi[kStreamMaxGroups];
 };
 
 // GEN: keys through per-sequence counts (query rows aligned to the end of
@@ -175,10 +179,11 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   // [seg_lo, seg_hi) of the tile, which the plan gives seg_n key tiles (a
   // sequence shorter than the plan assumes has fewer visible ones; the rest
   // are skipped) and which starts at unit seg_t0, has counter seg_tile and
-  // seg_before tiles before it in the list; this workgroup's range starts at
-  // unit seg_a.
+  // one piece in each of workgroups seg_w0..seg_w1; this workgroup's range
+  // starts at unit seg_a.
   auto run_qtile = [&](const int q0, const int bh, const int seg_lo, const int seg_hi, const int seg_n, const int seg_t0,
-                       const int seg_tile, const int seg_before, const int seg_a) __attribute__((always_inline)) {
+                       const int seg_tile, const int seg_w0, const int seg_w1,
+                       const int seg_a) __attribute__((always_inline)) {
   const int b = bh / Hq, h = bh - b * Hq;
   const int kvh = h / (Hq / Hkv);
   const bf16* kb = k + (size_t)b * kv.sb + (size_t)kvh * kv.sh;
@@ -609,10 +614,7 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   if constexpr (SPL) {
     // workgroups [w0, w1] share this tile; a piece of a shared tile hands its
     // state over (this workgroup's logical index is `item`, its first unit seg_a)
-    // owner of unit u: C(u) G / cost, with C(u) = u + tile_cost (tiles started before u)
-    const int G = total;
-    const int w0 = (seg_t0 + sp.tile_cost * seg_before) * G / sp.cost;
-    const int w1 = (seg_t0 + seg_n - 1 + sp.tile_cost * (seg_before + (seg_n > 1 ? 1 : 0))) * G / sp.cost;
+    const int w0 = seg_w0, w1 = seg_w1;
     if (w1 > w0) {
       // The pieces run on any XCD, and each XCD has its own L2, so the
       // hand-over goes through memory without whole-cache maintenance (an L2
@@ -756,19 +758,16 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
   if constexpr (SPL) {
     // this workgroup's units, piece by piece
     const int u_a = sp.wstart[item], u_end = sp.wstart[item + 1];
-    for (int u = u_a; u < u_end;) {
-      // the tile unit u falls in: (batch, head) block, then the last tile start <= u in the block
-      const int b_ = u / sp.per, r = u - b_ * sp.per;
-      int lo = 0, hi = nqt - 1;
-      while (lo < hi) {
-        const int mid = (lo + hi + 1) >> 1;
-        if (sp.tstart[mid] <= r) lo = mid;
-        else hi = mid - 1;
-      }
-      const int qt = grid::stream_pair_qt(lo, nqt);
-      const int t0 = b_ * sp.per + sp.tstart[lo], n = sp.tstart[lo + 1] - sp.tstart[lo], k0 = r - sp.tstart[lo];
+    // tiles in list order from the one holding the range's first unit; the
+    // first can be shared with earlier workgroups, the last with later ones
+    int ti = sp.wtile[item];
+    for (int u = u_a; u < u_end; ti++) {
+      const int b_ = ti / nqt, j = ti - b_ * nqt;
+      const int qt = grid::stream_pair_qt(j, nqt);
+      const int t0 = b_ * sp.per + sp.tstart[j], n = sp.tstart[j + 1] - sp.tstart[j], k0 = u - t0;
       const int k_hi = min(n, k0 + (u_end - u));
-      run_qtile(qt * BM, b_, k0, k_hi, n, t0, b_ * nqt + qt, b_ * nqt + lo, u_a);
+      const int w0 = t0 < u_a ? (int)sp.wlo[item] : item, w1 = t0 + n > u_end ? (int)sp.whi[item] : item;
+      run_qtile(qt * BM, b_, k0, k_hi, n, t0, b_ * nqt + qt, w0, w1, u_a);
       u += k_hi - k0;
     }
   } else {
@@ -776,8 +775,8 @@ __global__ __launch_bounds__(64 * NW, 2) void prefill_bf16_kernel(const bf16* __
     // heavy (late) causal query tiles first: with more workgroups than fit at
     // once, the light ones then fill in behind them
     const int qt_first = (npairs < nqt || causal) ? nqt - 1 - slot : slot;
-    run_qtile(qt_first * BM, bh, 0, 0, 0, 0, 0, 0, 0);
-    if (npairs < nqt && slot != nqt - 1 - slot) run_qtile(slot * BM, bh, 0, 0, 0, 0, 0, 0, 0);
+    run_qtile(qt_first * BM, bh, 0, 0, 0, 0, 0, 0, 0, 0);
+    if (npairs < nqt && slot != nqt - 1 - slot) run_qtile(slot * BM, bh, 0, 0, 0, 0, 0, 0, 0, 0);
   }
 }
 
@@ -822,7 +821,8 @@ constexpr int kSplitCounters = 1024;
 constexpr size_t kSplitCounterBytes = kSplitCounters * sizeof(int);
 constexpr int kStreamBM = 256;     // 8-wave workgroups, one per CU
 constexpr int kStreamMinUnits = 4;  // units per workgroup at least
-constexpr int kStreamTileCost = 2;  // cost of a tile start, in units (its prologue; best of 0-6 measured)
+constexpr int kStreamPieceCost = 2;  // cost of a piece, in units (its prologue)
+constexpr int kStreamMergeCost = 3;  // cost of merging a shared tile's pieces, in units
 // Whether the launcher pairs heavy and light causal tiles (the 8-wave grid, or
 // the 4-wave grid when it has 512 pairs): those grids are as fast as stream-K.
 bool paired_grid(long long bh, int Sq) {
@@ -840,7 +840,7 @@ bool paired_grid(long long bh, int Sq) {
 constexpr int kStreamMinShare = 16;
 int stream_off(int Sq, const KvSpec& kv) { return kv.lens ? kv.max_kv - Sq : 0; }
 grid::StreamPlan stream_plan_for(long long bh, int Sq, int off) {
-  return grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamTileCost, off);
+  return grid::stream_plan(bh, Sq, kStreamBM, kStreamMaxGroups, kStreamMinUnits, kStreamPieceCost, off);
 }
 bool split_applies(long long bh, int Sq, bool causal, const KvSpec& kv) {
   if (!causal || kv.window > 0 || kv.mask || paired_grid(bh, Sq)) return false;
@@ -853,6 +853,30 @@ bool split_applies(long long bh, int Sq, bool causal, const KvSpec& kv) {
   if (nqt > kStreamMaxTiles || bh * nqt > kSplitCounters) return false;
   const grid::StreamPlan p = stream_plan_for(bh, Sq, stream_off(Sq, kv));
   return p.ok && p.units >= (long long)kStreamMinShare * kStreamMaxGroups;
+}
+// The plan's tables for the last shape seen on this thread (serving loops
+// repeat shapes; the ranges come from a search over the greedy cover).
+SplitArgs stream_tables_cached(long long bh, int Sq, int off, const grid::StreamPlan& p) {
+  const long long key[3] = {bh, Sq, off};
+  thread_local long long last[3] = {-1, -1, -1};
+  thread_local SplitArgs tab;
+  if (!std::equal(key, key + 3, last)) {
+    const grid::StreamRanges r = grid::stream_ranges(p, bh, Sq, kStreamBM, kStreamMergeCost, off);
+    tab = SplitArgs{};
+    tab.per = p.per;
+    for (int j = 0, s = 0; j <= p.nqt; j++) {
+      tab.tstart[j] = s;
+      if (j < p.nqt) s += grid::stream_ntiles(Sq, grid::stream_pair_qt(j, p.nqt), kStreamBM, off);
+    }
+    for (int w = 0; w <= p.G; w++) tab.wstart[w] = r.wstart[w];
+    for (int w = 0; w < p.G; w++) {
+      tab.wtile[w] = (uint16_t)r.first_tile[w];
+      tab.wlo[w] = (uint8_t)r.lo_owner[w];
+      tab.whi[w] = (uint8_t)r.hi_owner[w];
+    }
+    std::copy(key, key + 3, last);
+  }
+  return tab;
 }
 size_t split_workspace_bytes(long long bh, int Sq, int D, const KvSpec& kv) {
   const grid::StreamPlan p = stream_plan_for(bh, Sq, stream_off(Sq, kv));
@@ -887,19 +911,10 @@ hipError_t launch_prefill_bf16_split(const void* q, const void* k, const void* v
   const int off = stream_off(Sq, kv);
   const grid::StreamPlan p = stream_plan_for(bh, Sq, off);
   const size_t nslots = 2 * (size_t)p.G;
-  SplitArgs sa;
+  SplitArgs sa = stream_tables_cached(bh, Sq, off, p);
   sa.cnt = reinterpret_cast<int*>(ws);
   sa.o = reinterpret_cast<uint32_t*>(static_cast<char*>(ws) + kSplitCounterBytes);
   sa.ml = reinterpret_cast<float*>(sa.o + nslots * kStreamBM * D / 2);
-  sa.per = p.per;
-  sa.cost = p.cost;
-  sa.tile_cost = p.tile_cost;
-  for (int j = 0, s = 0; j <= p.nqt; j++) {
-    sa.tstart[j] = s;
-    if (j < p.nqt) s += grid::stream_ntiles(Sq, grid::stream_pair_qt(j, p.nqt), kStreamBM, off);
-  }
-  for (int w = 0; w <= p.G; w++)
-    sa.wstart[w] = grid::stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, kStreamBM, p.tile_cost, off);
   const dim3 grid((unsigned)p.G), block(512);
 #define RCGQA_SPLIT_LAUNCH(DD, GG)                                                                                   \
   hipLaunchKernelGGL((prefill_bf16_kernel<DD, 8, GG, 1, 64, false, true>), grid, block, 0, st, (const bf16*)q,     \

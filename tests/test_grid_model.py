@@ -30,25 +30,29 @@ int main() {
       std::vector<double> w(k);
       for (auto& x : w) std::scanf("%lf", &x);
       std::printf("%.3f\n", busiest_cu(w, bh));
-    } else if (what[0] == 's') {                // stream bh Sq BM min_units tile_cost off: plan, then every piece
-      long long bh; int Sq, BM, mu, tc, off;
-      std::scanf("%lld %d %d %d %d %d", &bh, &Sq, &BM, &mu, &tc, &off);
-      const StreamPlan p = stream_plan(bh, Sq, BM, kCUs, mu, tc, off);
-      std::printf("%d %d %d %d %d\n", p.nqt, p.units, p.G, p.cost, p.ok ? 1 : 0);
-      for (int w = 0; w < p.G; w++) {   // the kernel's walk over its range
-        const int a = stream_start(w, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
-        const int e = stream_start(w + 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
-        for (int u = a; u < e;) {
-          const StreamTile t = stream_tile(u, p.nqt, p.per, Sq, BM, off);
-          const int k_hi = std::min(t.n, t.k + (e - u));
-          const int w0 = stream_owner(t.t0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
-          const int w1 = stream_owner(t.t0 + t.n - 1, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off);
-          const long long me = 2LL * w + (t.t0 > a ? 1 : 0);
-          const long long s0 =
-              2LL * w0 + (t.t0 > stream_start(w0, p.G, p.units, p.cost, p.nqt, p.per, Sq, BM, tc, off) ? 1 : 0);
-          std::printf("%d %d %d %d %d %d %d %d %lld %d %d %lld %d %d\n", w, t.bh, t.qt, t.k, k_hi, t.n, t.t0,
-                      t.tile, w1 > w0 ? me : -1LL, w0, w1, s0, a, e);
-          u += k_hi - t.k;
+    } else if (what[0] == 's') {                // stream bh Sq BM min_units piece_cost merge_cost off
+      long long bh; int Sq, BM, mu, pc, mc, off;
+      std::scanf("%lld %d %d %d %d %d %d", &bh, &Sq, &BM, &mu, &pc, &mc, &off);
+      const StreamPlan p = stream_plan(bh, Sq, BM, kCUs, mu, pc, off);
+      const StreamRanges r = stream_ranges(p, bh, Sq, BM, mc, off);
+      std::vector<int> tst(p.nqt + 1, 0);
+      for (int j = 0; j < p.nqt; j++) tst[j + 1] = tst[j] + stream_ntiles(Sq, stream_pair_qt(j, p.nqt), BM, off);
+      const int less = stream_cover(tst, p.nqt, p.per, p.units, p.G, pc, mc, r.budget - 1, nullptr);
+      std::printf("%d %d %d %d %lld %d\n", p.nqt, p.units, p.G, p.ok ? 1 : 0, r.budget, less);
+      for (int w = 0; w < p.G; w++) {   // the kernel's walk over its range, from the tables
+        const int a = r.wstart[w], e = r.wstart[w + 1];
+        std::printf("w %d %d %d\n", w, a, e);
+        int ti = r.first_tile[w];
+        for (int u = a; u < e; ti++) {
+          const int b = ti / p.nqt, j = ti - b * p.nqt, qt = stream_pair_qt(j, p.nqt);
+          const int t0 = b * p.per + tst[j], n = tst[j + 1] - tst[j], k0 = u - t0;
+          const int k_hi = std::min(n, k0 + (e - u));
+          const int w0 = t0 < a ? r.lo_owner[w] : w, w1 = t0 + n > e ? r.hi_owner[w] : w;
+          const long long me = 2LL * w + (t0 > a ? 1 : 0);
+          const long long s0 = 2LL * w0 + (t0 > r.wstart[w0] ? 1 : 0);
+          std::printf("%d %d %d %d %d %d %d %d %lld %d %d %lld %d %d\n", w, b, qt, k0, k_hi, n, t0, b * p.nqt + qt,
+                      w1 > w0 ? me : -1LL, w0, w1, s0, a, e);
+          u += k_hi - k0;
         }
       }
     } else {                                    // grid bh Sq causal nk window
@@ -142,30 +146,32 @@ def test_grid_choice_on_timed_shapes(model, shape, four):
     assert int(got[1]) == (((nqt2 + 1) // 2 if paired else nqt2) if four else nqt4)
 
 
-@pytest.mark.parametrize("bh,Sq,BM,mu,tc,off", [(8, 4096, 256, 4, 3, 0), (8, 2100, 256, 4, 3, 0), (1, 1, 256, 4, 3, 0),
-                                                 (1, 257, 256, 4, 3, 0), (4, 8192, 256, 4, 3, 0),
-                                                 (16, 300, 256, 4, 3, 0), (2, 64, 256, 1, 0, 0),
-                                                 (8, 1024, 128, 4, 2, 0), (3, 5000, 256, 7, 5, 0),
-                                                 (64, 4096, 256, 4, 3, 0), (64, 512, 256, 4, 2, 4096),
-                                                 (8, 700, 256, 4, 2, 3000), (3, 1, 256, 4, 2, 77)])
-def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc, off):
+@pytest.mark.parametrize("bh,Sq,BM,mu,pc,mc,off", [
+    (8, 4096, 256, 4, 2, 3, 0), (8, 2100, 256, 4, 2, 3, 0), (1, 1, 256, 4, 2, 3, 0), (1, 257, 256, 4, 2, 3, 0),
+    (4, 8192, 256, 4, 2, 3, 0), (16, 300, 256, 4, 2, 3, 0), (2, 64, 256, 1, 0, 0, 0), (8, 1024, 128, 4, 2, 0, 0),
+    (3, 5000, 256, 7, 5, 4, 0), (64, 4096, 256, 4, 2, 3, 0), (64, 512, 256, 4, 2, 3, 4096),
+    (8, 700, 256, 4, 2, 6, 3000), (3, 1, 256, 4, 2, 3, 77), (1, 32768, 256, 16, 2, 3, 0),
+    (4, 16384, 256, 16, 2, 3, 0), (2, 512, 256, 4, 2, 3, 15872), (1, 2048, 256, 4, 2, 3, 6144)])
+def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, pc, mc, off):
     """The stream-K grid (causal problems on unpaired grids, plain or against a
-    cache of `off` earlier tokens): workgroups take contiguous,
-    non-empty ranges of the unit list (batch-head, then query tiles in heavy /
-    light pairs, then key tile) that balance units plus tc per tile started;
-    the pieces cover every key tile a query tile sees under the causal rule
-    exactly once; a tile shared by several workgroups gives each of them a
-    distinct partial slot (at most two per workgroup, the first piece of a
-    range in slot 2w, the last in 2w + 1), and the merge order (workgroups
-    w0..w1, slot s0 for w0 and 2w after) is the key order."""
-    out = model([f"s {bh} {Sq} {BM} {mu} {tc} {off}"])
-    nqt, units, G, cost, ok = (int(x) for x in out[0].split())
-    assert ok == (cost * (G + 1) < 2 ** 31) and ok
-    rows = [tuple(int(x) for x in r.split()) for r in out[1:]]
+    cache of `off` earlier tokens): workgroups take contiguous ranges of the
+    unit list (batch-head, then query tiles in heavy / light pairs, then key
+    tile), non-empty but for trailing ones, each within the budget (one per
+    unit, pc per tile touched, mc when the range ends inside a tile), which
+    is the least one whose greedy cover fits G workgroups; the pieces cover
+    every key tile a query tile sees under the causal rule exactly once; a
+    tile shared by several workgroups gives each of them a distinct partial
+    slot (at most two per workgroup, the first piece of a range in slot 2w,
+    the last in 2w + 1), its owners w0..w1 from the tables are the brute-force
+    owners, and the merge order (w0..w1, slot s0 for w0 and 2w after) is the
+    key order."""
+    out = model([f"s {bh} {Sq} {BM} {mu} {pc} {mc} {off}"])
+    nqt, units, G, ok, budget, less = (int(x) for x in out[0].split())
+    assert ok
     # query row i at key position i + off: tile qt sees keys below min(Sq, BM (qt + 1)) + off
     ntiles = [(min(Sq, BM * (qt + 1)) + off + 63) // 64 for qt in range(nqt)]
-    assert nqt == -(-Sq // BM) and units == bh * sum(ntiles) and cost == units + tc * bh * nqt
-    assert G == max(1, min(256, units // max(mu, tc + 2)))
+    assert nqt == -(-Sq // BM) and units == bh * sum(ntiles)
+    assert G == max(1, min(256, units // max(mu, pc + 2)))
     # list order: (batch, head), then query tiles in heavy / light pairs
     pairs = []
     for p in range((nqt + 1) // 2):
@@ -175,29 +181,51 @@ def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc, off):
     assert sorted(pairs) == list(range(nqt))
     order = [(b, qt) for b in range(bh) for qt in pairs]
     t0 = {}
+    tile_at = np.zeros(units, dtype=np.int64)   # list index of the tile holding each unit
     acc = 0
-    starts = []
-    for b, qt in order:
+    for i, (b, qt) in enumerate(order):
         t0[(b, qt)] = acc
-        starts.append(acc)
+        tile_at[acc:acc + ntiles[qt]] = i
         acc += ntiles[qt]
-    # cost of every unit boundary, counted directly: C(u) = u + tc * (tiles starting before u)
-    started = np.zeros(units + 1, dtype=np.int64)
-    for x in starts:
-        started[x + 1:] += 1
-    Cu = np.arange(units + 1, dtype=np.int64) + tc * started
-
-    def C(u):
-        return int(Cu[u])
+    ends = np.cumsum([ntiles[qt] for _, qt in order])
     bounds = {}
+    rows = []
+    for line in out[1:]:
+        f = line.split()
+        if f[0] == "w":
+            bounds[int(f[1])] = (int(f[2]), int(f[3]))
+        else:
+            rows.append(tuple(int(x) for x in f))
+    # ranges: contiguous from 0 to units, non-empty but for trailing empty ones
+    assert sorted(bounds) == list(range(G))
+    assert bounds[0][0] == 0 and bounds[G - 1][1] == units
+    used = [w for w in range(G) if bounds[w][0] < bounds[w][1]]
+    assert used == list(range(len(used))) and len(used) >= 1
+    for w in range(G - 1):
+        assert bounds[w][1] == bounds[w + 1][0]
+    owner = np.zeros(units, dtype=np.int64)
+    for w in used:
+        owner[bounds[w][0]:bounds[w][1]] = w
+
+    def cost(a, e):
+        t = tile_at[a:e]
+        c = (e - a) + pc * (int(t[-1]) - int(t[0]) + 1)
+        return c + (mc if e < ends[t[-1]] else 0)
+    # every range within the budget; one less needs more than G workgroups
+    for w in used:
+        assert cost(*bounds[w]) <= budget
+    assert less > G
+    total = units + pc * len(order)
+    assert budget <= total / G + 2 * (pc + mc) + 2
     cover = {}
     slots = {}
     per_wg = {}
     for w, b, qt, klo, khi, n, t, tile, me, w0, w1, s0, a, e in rows:
-        bounds[w] = (a, e)
+        assert (a, e) == bounds[w]
         assert 0 <= b < bh and 0 <= qt < nqt and n == ntiles[qt]
         assert t == t0[(b, qt)] and tile == b * nqt + qt
         assert 0 <= klo < khi <= n and a <= t + klo and t + khi <= e
+        assert (w0, w1) == (owner[t], owner[t + n - 1])
         per_wg[w] = per_wg.get(w, 0) + khi - klo
         cover.setdefault((b, qt), []).append((klo, khi, w, me, w0, w1, s0))
         if w1 > w0:
@@ -206,15 +234,8 @@ def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc, off):
             slots[me] = (b, qt)
         else:
             assert me == -1 and (klo, khi) == (0, n)
-    # ranges: contiguous, non-empty, each the brute-force first unit with C(u) G >= w cost
-    assert sorted(bounds) == list(range(G))
-    for w in range(G):
-        a, e = bounds[w]
-        assert a < e and per_wg[w] == e - a
-        assert a == int(np.nonzero(Cu * G >= w * cost)[0][0])
-        if w + 1 < G:
-            assert bounds[w + 1][0] == e
-    assert bounds[0][0] == 0 and bounds[G - 1][1] == units
+    for w in used:
+        assert per_wg[w] == bounds[w][1] - bounds[w][0]
     assert len(cover) == bh * nqt
     for (b, qt), pieces in cover.items():
         pieces.sort()
@@ -227,7 +248,3 @@ def test_stream_plan_covers_every_tile_once(model, bh, Sq, BM, mu, tc, off):
             s0 = pieces[0][6]
             merge_slots = [s0] + [2 * w for w in range(w0 + 1, w1 + 1)]
             assert merge_slots == [p[3] for p in pieces]
-    # balance: no range costs more than the mean plus one tile start and one unit
-    for w in range(G):
-        a, e = bounds[w]
-        assert C(e) - C(a) <= cost / G + tc + 1

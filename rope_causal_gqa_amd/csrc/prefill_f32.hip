@@ -7,7 +7,10 @@
 // Design: one wave per 64 query rows of one (batch, head); each lane owns one
 // query row (q and the fp32 accumulator in registers) and walks the keys with
 // an online softmax using the accurate expf.  K/V tiles of 32 keys are staged
-// in LDS and read as wave-wide broadcasts.  Causal tiles past the block's last
+// in LDS and read as wave-wide broadcasts, a whole K or V row per batch of
+// reads; dot products run as four partial sums.  (A lone wave hides no
+// latency by itself: without these, each LDS read and each FMA of a chain
+// was waited out.)  Causal tiles past the block's last
 // row (and, with a sliding window, before its first window) are never loaded.
 // Keys come through strides and per-sequence counts, so the same kernel serves
 // chunked / variable-length prefill against a cache; an optional additive
@@ -77,16 +80,25 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const float* __restrict
     __syncthreads();
     if (!live) continue;
     const int jn = min(BN, nk - kv0);
+    // Each key's K row, then its V row, is read into registers in one batch
+    // (a lone wave would otherwise wait out each LDS read in turn).
     for (int j = 0; j < jn; j++) {
       const int key = kv0 + j;
       if (causal && key > pos) break;
       if (W > 0 && key <= pos - W) continue;
-      const float* kr = reinterpret_cast<const float*>(sk) + j * D;
-      const float* vr = reinterpret_cast<const float*>(sv) + j * D;
-      float dot = 0.f;
+      float4 kr[D / 4];
 #pragma unroll
-      for (int d = 0; d < D; d++) dot = fmaf(qr[d], kr[d], dot);
-      float s = dot * scale;
+      for (int c = 0; c < D / 4; c++) kr[c] = sk[j * (D / 4) + c];
+      // four independent partial sums: the dependent FMA chain is D / 4 long
+      float d4[4] = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int c = 0; c < D / 4; c++) {
+        d4[0] = fmaf(qr[4 * c], kr[c].x, d4[0]);
+        d4[1] = fmaf(qr[4 * c + 1], kr[c].y, d4[1]);
+        d4[2] = fmaf(qr[4 * c + 2], kr[c].z, d4[2]);
+        d4[3] = fmaf(qr[4 * c + 3], kr[c].w, d4[3]);
+      }
+      float s = ((d4[0] + d4[1]) + (d4[2] + d4[3])) * scale;
       if (mrow) {
         s += mrow[key];
         if (!(s > -INFINITY)) continue;  // a masked key: no weight (and no -inf - -inf)
@@ -100,6 +112,9 @@ __global__ __launch_bounds__(64) void prefill_f32_kernel(const float* __restrict
       }
       const float p = expf(s - m);
       l += p;
+#pragma unroll
+      for (int c = 0; c < D / 4; c++) kr[c] = sv[j * (D / 4) + c];  // the V row, in K's registers
+      const float* vr = reinterpret_cast<const float*>(kr);
 #pragma unroll
       for (int d = 0; d < D; d++) acc[d] = fmaf(p, vr[d], acc[d]);
     }

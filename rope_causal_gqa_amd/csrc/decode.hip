@@ -116,26 +116,30 @@ __global__ __launch_bounds__(D) void decode_merge_kernel(const float* __restrict
 }
 
 // Pass 1, bf16 form, on matrix cores.  One workgroup = DW waves handles one
-// split of KCH keys of one (batch, KV head) for all G <= 16 query heads of the
-// group, so each K/V row is read from HBM once per group.  Each wave streams
+// split of kch keys (2048, or 4096 on large grids) of one (batch, KV head)
+// for all G <= 16 query heads of the group, so each K/V row is read from HBM
+// once per group.  Each wave streams
 // its own 32-key tiles (tiles w, w+DW, ... of the split) through a private LDS
 // region, with the next tile prefetched into registers while the current one
 // is computed; waves never wait for each other until the final combine.  The
 // cache is read with non-temporal loads: it is streamed once per call, so
 // keeping it out of L2 / Infinity Cache leaves them to the partial states.
-// Defaults (2048-key splits, 8 waves, non-temporal) were picked by a sweep on
-// the B=64 Hq=64 Hkv=8 D=128 workload with lengths in [512, 8192]:
-// 512/4/temporal 242 us, 1024/8/temporal 235 us, 2048/8/non-temporal 208 us.
+// 8 waves and non-temporal loads were picked by a sweep on the B=64 Hq=64
+// Hkv=8 D=128 workload with lengths in [512, 8192]: 512/4/temporal 242 us,
+// 1024/8/temporal 235 us, 2048/8/non-temporal 208 us (the split length is
+// chosen at launch, see launch_decode_bf16).
 //   S^T (32 keys x 16 heads) = K Q^T   v_mfma_f32_16x16x32_bf16, K from LDS
 //   O^T (D x 16 heads)      += V^T P^T  same MFMA, V^T via the LDS transpose read
 // In both outputs a lane owns one head (lane % 16), so the online-softmax
 // rescale is one multiply per accumulator.  The DW waves' states are combined
 // in LDS and written as one partial state per (split, head).
 namespace {
-constexpr int KCH = 2048;  // keys per split (>= KC, so the workspace bound holds)
+constexpr int KCH = 2048;  // keys per split, the shorter length (>= KC, so the workspace bound holds)
+constexpr int KCH_LONG = 2 * KCH;  // keys per split when the grid stays large (see the launcher)
+constexpr long long kDecodeLongSplitGroups = 512;  // two workgroups per CU of the 256
 constexpr int TK = 32;     // keys per wave tile
 constexpr int DW = 8;      // waves per workgroup
-static_assert(KCH >= KC && KCH % TK == 0, "split must be a multiple of the tile and at least KC");
+static_assert(KCH >= KC && KCH % TK == 0 && KCH_LONG % TK == 0, "split must be a multiple of the tile and at least KC");
 }
 
 template <int D>
@@ -144,7 +148,7 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
                                                              const bf16* __restrict__ vc,
                                                              const int32_t* __restrict__ kv_lens,
                                                              float* __restrict__ ws, int Hq, int Hkv, int max_kv,
-                                                             int nsplit, float c_log2) {
+                                                             int nsplit, int kch, float c_log2) {
   constexpr int CH = D / 8;         // 16-byte chunks per row
   constexpr int SW = CH - 1;        // swizzle mask
   constexpr int KSTEP = D / 32;     // k-steps of Q K^T
@@ -155,9 +159,9 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
 
   const int split = blockIdx.x, kvh = blockIdx.y, b = blockIdx.z;
   const int L = min(max(kv_lens[b], 0), max_kv);
-  const int k0 = split * KCH;
+  const int k0 = split * kch;
   if (k0 >= L) return;  // uniform: nothing in this split
-  const int kend = min(L, k0 + KCH);
+  const int kend = min(L, k0 + kch);
   const int ntile = (kend - k0 + TK - 1) / TK;
   const int G = Hq / Hkv;
 
@@ -329,11 +333,11 @@ __global__ __launch_bounds__(64 * DW) void decode_mfma_kernel(const bf16* __rest
 template <int D>
 __global__ __launch_bounds__(D) void decode_merge2_kernel(const float* __restrict__ ws,
                                                           const int32_t* __restrict__ kv_lens, bf16* __restrict__ out,
-                                                          int Hq, int max_kv, int nsplit) {
+                                                          int Hq, int max_kv, int nsplit, int kch) {
   constexpr int MB = 8;
   const int h = blockIdx.x, b = blockIdx.y, d = threadIdx.x;
   const int L = min(max(kv_lens[b], 0), max_kv);
-  const int ns = (L + KCH - 1) / KCH;
+  const int ns = (L + kch - 1) / kch;
   const float* src = ws + ((size_t)b * Hq + h) * nsplit * (D + 2);
   float M = -INFINITY, den = 0.f, num = 0.f;
   for (int c0 = 0; c0 < ns; c0 += MB) {
@@ -377,12 +381,18 @@ static void launch_decode_t(const void* q, const void* kc, const void* vc, const
 template <int D>
 static void launch_decode_bf16(const void* q, const void* kc, const void* vc, const int32_t* kv_lens, void* out,
                                int B, int Hq, int Hkv, int max_kv, float scale, void* ws, hipStream_t st) {
-  const int nsplit = (max_kv + KCH - 1) / KCH;
+  // Longer splits halve the partial states and the workgroups' fixed costs,
+  // but each workgroup (one per CU: its LDS takes most of a CU's) then
+  // streams twice the keys, so they are taken only while the grid keeps at
+  // least two workgroups per CU.  On B=64 Hq=64 Hkv=8 D=128 with lengths in
+  // [512, 8192]: 1024 keys 5830 GB/s, 2048 6030, 3072 6020, 4096 6100, 6144 4740.
+  const int kch = (long long)B * Hkv * ((max_kv + KCH_LONG - 1) / KCH_LONG) >= kDecodeLongSplitGroups ? KCH_LONG : KCH;
+  const int nsplit = (max_kv + kch - 1) / kch;
   const float c_log2 = (float)((double)scale * 1.4426950408889634);
   hipLaunchKernelGGL(decode_mfma_kernel<D>, dim3(nsplit, Hkv, B), dim3(64 * DW), 0, st, (const bf16*)q,
-                     (const bf16*)kc, (const bf16*)vc, kv_lens, (float*)ws, Hq, Hkv, max_kv, nsplit, c_log2);
+                     (const bf16*)kc, (const bf16*)vc, kv_lens, (float*)ws, Hq, Hkv, max_kv, nsplit, kch, c_log2);
   hipLaunchKernelGGL(decode_merge2_kernel<D>, dim3(Hq, B), dim3(D), 0, st, (const float*)ws, kv_lens, (bf16*)out, Hq,
-                     max_kv, nsplit);
+                     max_kv, nsplit, kch);
 }
 
 hipError_t launch_decode(const void* q, const void* kc, const void* vc, const int32_t* kv_lens, void* out, int B,

@@ -24,8 +24,10 @@ shapes that the launcher runs on unpaired grids, and attn_prefill_cache_ws again
 attn_prefill_cache on two chunked prefills; `fused_rope_prefill` / `fused_rope_decode` time the fused RoPE
 entry points against the separate calls on the same workloads; `ntk_rope`
 times rope_apply at an NTK-aware scaled base; `masked_prefill` times
-attn_prefill_masked (causal plus a key-padding mask) on LLaMA-7B-shaped heads.  `cpu_baseline` times the float64 oracle on a bounded sample on
-the host cores.
+attn_prefill_masked (causal plus a key-padding mask) on LLaMA-7B-shaped heads;
+`small_configs` times RoPE and attention on the three small workloads (tiny fp32
+GQA, S=128 MHA unmasked and causal with RoPE).  `cpu_baseline` times the float64
+oracle on a bounded sample on the host cores.
 
 Before the W warm-up steps the step runs untimed for --settle-s seconds
 (default 2): under sustained MFMA load the GPU lowers its clock within the
@@ -268,6 +270,31 @@ def _next_rows(R, dev, stream):
     return out
 
 
+def _small_rows(R, dev, stream):
+    """The three small workloads (tiny fp32 GQA prefill; S=128 MHA bf16 unmasked, and
+    causal with RoPE), outside the timed step: RoPE and attention timed as separate
+    launches on the seeded inputs (RoPE rotates them in place again on every launch,
+    which does not change its cost).  Parity configurations, not bench lines: at
+    these sizes a launch is bound by latency, not by the MFMA or HBM rooflines."""
+    import torch
+    from rope_causal_gqa_amd import workloads as W
+    rows = []
+    for name in ("c1", "c2a", "c2b"):
+        w = W.WORKLOADS[name]
+        if w.dtype == "fp32":
+            q, k, v = (torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in W.prefill_inputs(w))
+        else:
+            q, k, v = (torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).view(torch.bfloat16).to(dev)
+                       for a in W.prefill_inputs(w))
+        o = torch.empty_like(q)
+        rope_ms = _time_launches(lambda: R.rope_apply(q, k, None, w.theta, w.factor), stream) if w.rope else 0.0
+        attn_ms = _time_launches(lambda: R.attn_prefill(q, k, v, o, causal=w.causal, scale=w.scale), stream)
+        rows.append({"workload": f"{name}: {w.name}, B={w.B} S={w.S} Hq={w.Hq} Hkv={w.Hkv} D={w.D}",
+                     "dtype": w.dtype, "rope_us": round(rope_ms * 1e3, 1), "attention_us": round(attn_ms * 1e3, 1),
+                     "attention_tflops": round(w.flops() / (attn_ms * 1e-3) / 1e12, 2)})
+    return rows
+
+
 def _fused_rows(R, wp, wd, q, k, v, out, dq, dkn, dvn, kc, vc, ctx_d, lens_d, pos_d, dout, ws, stream):
     """The fused RoPE paths against the separate calls, on the same two workloads
     (outside the timed step):
@@ -443,9 +470,10 @@ def main():
     pre_tflops = pre_flops / (pre_ms.mean() * 1e-3) / 1e12
     dec_gbps = dec_bytes / (dec_ms.mean() * 1e-3) / 1e9
     rope_bytes = 2.0 * wp.B * wp.S * (wp.Hq + wp.Hkv) * wp.D * 2
-    extras, fused = {}, {}
+    extras, fused, small = {}, {}, None
     if not args.no_extras:
         extras = _next_rows(R, dev, stream)
+        small = _small_rows(R, dev, stream)
         fused = _fused_rows(R, wp, wd, q, k, v, out, dq, dkn, dvn, caches[0][0], caches[0][1], ctx_d, lens_d,
                             pos_d, dout, ws, stream)
     res = {
@@ -486,6 +514,7 @@ def main():
         "fused_rope_prefill": fused.get("fused_rope_prefill"),
         "fused_rope_decode": fused.get("fused_rope_decode"),
         "ntk_rope": fused.get("ntk_rope"),
+        "small_configs": small,
         "cpu_baseline": None,
     }
     if not args.no_cpu_baseline:

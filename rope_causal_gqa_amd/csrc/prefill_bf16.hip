@@ -968,7 +968,11 @@ hipError_t launch_prefill_bf16(const void* q, const void* k, const void* v, void
   const bool short_window = kv.window > 0 && kv.window < 2048;
   // the 8-wave grid stages mask tiles in LDS with 16-byte loads: rows of a multiple of 8 entries
   const bool mask_ok = !kv.mask || (kv.msr % 8 == 0 && kv.msr >= 8);
-  if (causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512 && !short_window && mask_ok) {
+  // With D = 64 a K/V tile is half the bytes, and the 4-wave grid measured as
+  // fast or faster (interleaved, bit-identical: B=2 S=4096 Hq=32 +2%, B=1
+  // S=4096 Hq=32 Hkv=8 +0.3%, B=4 S=2048 Hq=32 +5%, B=1 S=8192 Hq=16 +0.3%);
+  // with D = 128 it is 4% slower on the same shapes.
+  if (D == 128 && causal && nqt8 > 1 && bh * ((nqt8 + 1) / 2) >= 512 && !short_window && mask_ok) {
     launch_nw<8, 1>(q, k, v, out, B, Sq, Hq, Hkv, D, causal, c_log2, (nqt8 + 1) / 2, kv, q_rope, st);
   } else {
     const bool pair4 = causal && nqt4 > 1 && bh * ((nqt4 + 1) / 2) >= 512;
